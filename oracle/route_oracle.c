@@ -1,0 +1,266 @@
+/*
+ * route_oracle.c -- plain, slow, obviously-correct CPU reference for MoE
+ * routing top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never calls it and shares no code
+ * with it.
+ *
+ * Everything is computed in double precision, one token row at a time, in the
+ * order the pages describe the method.  Sorting uses the C library qsort with
+ * an explicit (score desc, index asc) comparator.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [ROUTING]  "[SGLang] MoE routing: token-to-expert assignment algorithms"
+ *              (blog.secrett2633.cloud/opensource/sglang/moe-routing)
+ *              sections 2 (softmax Top-K), 3 (Grouped Top-K, DeepSeek style),
+ *              4 (Biased Grouped Top-K with correction_bias),
+ *              5 (Fused MoE Router).
+ *   [AITER]    "[sglang] SGLang MoE routing optimisation: using
+ *              aiter.biased_grouped_topk on AMD GPUs"
+ *              (sglang PR 23611 analysis), section "Code analysis".
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *   - expert ties are broken by the lower expert index, group ties by the
+ *     lower group index;
+ *   - the K chosen ids are emitted in (selection score desc, index asc) order;
+ *   - experts of dropped groups are not candidates at all (equivalent to a
+ *     -inf mask);
+ *   - with a correction bias, selection uses sigmoid + bias while the emitted
+ *     weight is the unbiased sigmoid score;
+ *   - renormalisation divides the K weights by their plain sum.
+ *
+ * Parity status: every function here is pinned by the CPU tests
+ * (hand-worked cases, closed forms, brute force on tiny inputs, invariants,
+ * and a library matmul for the router projection).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F64 2
+
+#define OR_SOFTMAX 0
+#define OR_SIGMOID 1
+
+#define OR_GROUP_MAX 0     /* DeepSeek-V2 style: group score = max     */
+#define OR_GROUP_TOP2SUM 1 /* DeepSeek-V3 style: sum of the top-2      */
+
+/* Widen one logit to double.  bf16 is the upper half of an IEEE binary32,
+ * so putting its 16 bits on top of 16 zero bits gives the exact value. */
+static double load_logit(const void* base, int dtype, int64_t i) {
+    if (dtype == OR_F32) return (double)((const float*)base)[i];
+    if (dtype == OR_F64) return ((const double*)base)[i];
+    {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+}
+
+typedef struct {
+    double key;
+    int idx;
+} keyed_t;
+
+/* Larger key first; equal keys by ascending index. */
+static int cmp_desc_then_index(const void* a, const void* b) {
+    const keyed_t* x = (const keyed_t*)a;
+    const keyed_t* y = (const keyed_t*)b;
+    if (x->key > y->key) return -1;
+    if (x->key < y->key) return 1;
+    return (x->idx > y->idx) - (x->idx < y->idx);
+}
+
+/*
+ * Scores of one row.
+ * softmax  ([ROUTING] section 2 and the first line of section 3): the
+ *          probability of expert i is exp(x_i - max x) / sum_j exp(x_j - max x),
+ *          taken over all E experts.
+ * sigmoid  ([ROUTING] section 4; [AITER] sigmoid scoring): 1 / (1 + exp(-x_i)).
+ * The selection score adds the per-expert correction bias when one is given
+ * ([ROUTING] section 4: scores_for_choice = scores + bias).
+ */
+int oracle_row_scores(const void* logits, int dtype, int E, const float* bias,
+                      int scoring, double* s, double* c) {
+    int i;
+    if (E <= 0 || (scoring != OR_SOFTMAX && scoring != OR_SIGMOID)) return 1;
+    if (scoring == OR_SOFTMAX) {
+        double mx = load_logit(logits, dtype, 0), sum = 0.0;
+        for (i = 1; i < E; ++i) {
+            double x = load_logit(logits, dtype, i);
+            if (x > mx) mx = x;
+        }
+        for (i = 0; i < E; ++i) {
+            s[i] = exp(load_logit(logits, dtype, i) - mx);
+            sum += s[i];
+        }
+        for (i = 0; i < E; ++i) s[i] = s[i] / sum;
+    } else {
+        for (i = 0; i < E; ++i) s[i] = 1.0 / (1.0 + exp(-load_logit(logits, dtype, i)));
+    }
+    for (i = 0; i < E; ++i) c[i] = s[i] + (bias ? (double)bias[i] : 0.0);
+    return 0;
+}
+
+/*
+ * Group scores of one row.  Groups are contiguous blocks of E/G experts, as
+ * the pages' view(num_token, num_expert_group, -1) reshape implies.
+ *   max rule     ([ROUTING] section 3): the largest selection score in the group.
+ *   top-2 rule   ([ROUTING] section 4): the sum of the two largest selection
+ *                scores in the group.
+ */
+int oracle_group_scores(const double* c, int E, int G, int group_rule, double* h) {
+    int g, j, gs;
+    keyed_t* tmp;
+    if (G <= 0 || E % G != 0) return 1;
+    gs = E / G;
+    if (group_rule == OR_GROUP_TOP2SUM && gs < 2) return 1;
+    tmp = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)gs);
+    if (!tmp) return 1;
+    for (g = 0; g < G; ++g) {
+        for (j = 0; j < gs; ++j) {
+            tmp[j].key = c[g * gs + j];
+            tmp[j].idx = g * gs + j;
+        }
+        qsort(tmp, (size_t)gs, sizeof(keyed_t), cmp_desc_then_index);
+        h[g] = (group_rule == OR_GROUP_MAX) ? tmp[0].key : tmp[0].key + tmp[1].key;
+    }
+    free(tmp);
+    return 0;
+}
+
+/*
+ * Route M rows.
+ *   1. scores s and selection scores c            (oracle_row_scores)
+ *   2. group scores h, then keep the TG groups with the largest h
+ *      ([ROUTING] section 3: topk over group scores, then a mask that keeps
+ *      only the experts of the chosen groups); G == 1 keeps everything.
+ *   3. the K candidates with the largest c, in (c desc, index asc) order
+ *      ([ROUTING] section 3: topk over the masked scores).
+ *   4. weight k = s of the chosen expert (unbiased, [ROUTING] section 4 says
+ *      the bias only steers which experts are chosen); with renormalize the
+ *      K weights are divided by their sum ([ROUTING] section 2).
+ * Optional diagnostics per row (gaps, may be NULL), three doubles:
+ *   gaps[0] = c of the K-th pick minus c of the best unpicked candidate
+ *             (+inf when there is no unpicked candidate);
+ *   gaps[1] = smallest difference between consecutive picks (+inf if K == 1);
+ *   gaps[2] = h of the TG-th kept group minus h of the best dropped group
+ *             (+inf when no group is dropped).
+ * Returns 0 on success, 1 on an argument the method does not define.
+ */
+int oracle_route(const void* logits, int dtype, int64_t M, int E, const float* bias,
+                 int scoring, int group_rule, int G, int TG, int K, int renormalize,
+                 float* weights, int32_t* ids, double* gaps) {
+    int64_t m;
+    int rc = 0;
+    double *s, *c, *h;
+    keyed_t *gk, *cand;
+    unsigned char* kept;
+    size_t esz = (dtype == OR_F32) ? 4 : (dtype == OR_BF16) ? 2 : 8;
+
+    if (M < 0 || E <= 0 || G <= 0 || E % G != 0 || TG < 1 || TG > G || K < 1) return 1;
+    if (K > TG * (E / G)) return 1;
+    if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64) return 1;
+    if (group_rule != OR_GROUP_MAX && group_rule != OR_GROUP_TOP2SUM) return 1;
+    if (G > 1 && group_rule == OR_GROUP_TOP2SUM && E / G < 2) return 1;
+
+    s = (double*)malloc(sizeof(double) * (size_t)E);
+    c = (double*)malloc(sizeof(double) * (size_t)E);
+    h = (double*)malloc(sizeof(double) * (size_t)G);
+    gk = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)G);
+    cand = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)E);
+    kept = (unsigned char*)malloc((size_t)G);
+    if (!s || !c || !h || !gk || !cand || !kept) {
+        rc = 1;
+        goto done;
+    }
+
+    for (m = 0; m < M; ++m) {
+        const void* row = (const char*)logits + (size_t)m * (size_t)E * esz;
+        int g, i, k, n = 0, gs = E / G;
+        double wsum = 0.0;
+
+        if (oracle_row_scores(row, dtype, E, bias, scoring, s, c)) { rc = 1; goto done; }
+
+        /* group selection */
+        if (G > 1) {
+            if (oracle_group_scores(c, E, G, group_rule, h)) { rc = 1; goto done; }
+            for (g = 0; g < G; ++g) { gk[g].key = h[g]; gk[g].idx = g; kept[g] = 0; }
+            qsort(gk, (size_t)G, sizeof(keyed_t), cmp_desc_then_index);
+            for (g = 0; g < TG; ++g) kept[gk[g].idx] = 1;
+        } else {
+            kept[0] = 1;
+        }
+
+        /* candidates = experts of kept groups, sorted (c desc, index asc) */
+        for (i = 0; i < E; ++i) {
+            if (!kept[i / gs]) continue;
+            cand[n].key = c[i];
+            cand[n].idx = i;
+            ++n;
+        }
+        qsort(cand, (size_t)n, sizeof(keyed_t), cmp_desc_then_index);
+
+        for (k = 0; k < K; ++k) wsum += s[cand[k].idx];
+        for (k = 0; k < K; ++k) {
+            double w = s[cand[k].idx];
+            if (renormalize) w = w / wsum;
+            weights[m * K + k] = (float)w;
+            ids[m * K + k] = (int32_t)cand[k].idx;
+        }
+
+        if (gaps) {
+            double og = INFINITY;
+            gaps[m * 3 + 0] = (n > K) ? cand[K - 1].key - cand[K].key : INFINITY;
+            for (k = 0; k + 1 < K; ++k) {
+                double d = cand[k].key - cand[k + 1].key;
+                if (d < og) og = d;
+            }
+            gaps[m * 3 + 1] = og;
+            gaps[m * 3 + 2] = (G > 1 && TG < G) ? gk[TG - 1].key - gk[TG].key : INFINITY;
+        }
+    }
+
+done:
+    free(s);
+    free(c);
+    free(h);
+    free(gk);
+    free(cand);
+    free(kept);
+    return rc;
+}
+
+/*
+ * Router projection of the fused router ([ROUTING] section 5): the logit of
+ * expert e for token m is the dot product of the token's hidden vector with
+ * the expert's router weights, accumulated in high precision.  Both operands
+ * are bf16 (raw 16-bit patterns); each product of two bf16 values is exact in
+ * double and the sum runs over h in ascending order.  The router weight is
+ * stored [H, E] (row h holds the weights of every expert for hidden unit h).
+ */
+int oracle_router_logits(const uint16_t* hidden, const uint16_t* w, int64_t M, int H,
+                         int E, double* logits) {
+    int64_t m;
+    int e, hh;
+    if (M < 0 || H <= 0 || E <= 0) return 1;
+    for (m = 0; m < M; ++m) {
+        for (e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (hh = 0; hh < H; ++hh) {
+                double a = load_logit(hidden, OR_BF16, m * (int64_t)H + hh);
+                double b = load_logit(w, OR_BF16, (int64_t)hh * E + e);
+                acc += a * b;
+            }
+            logits[m * E + e] = acc;
+        }
+    }
+    return 0;
+}
