@@ -1,0 +1,163 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE routing library
+ * (libmoe_route.so).
+ *
+ * Per token row of router logits, the library scores every expert, optionally
+ * keeps only the best expert groups, picks the top-K experts among the
+ * survivors, and writes fp32 weights and int32 expert ids.  The operations are
+ * defined on these pages:
+ *
+ *   [ROUTING] "[SGLang] MoE routing: token-to-expert assignment algorithms"
+ *             (blog.secrett2633.cloud/opensource/sglang/moe-routing)
+ *   [AITER]   "[sglang] SGLang MoE routing optimisation: using
+ *             aiter.biased_grouped_topk on AMD GPUs" (sglang PR 23611 analysis)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every pointer is a DEVICE pointer owned by the caller.  Tensors are
+ *           dense, row-major, with no padding between rows.  Outputs are
+ *           preallocated by the caller and filled in place, as the pages' call
+ *           sites do ([ROUTING] section 2; [AITER] section "Code analysis").
+ * Outputs.  topk_weights: float32 [num_tokens, top_k].
+ *           topk_ids:     int32   [num_tokens, top_k], row r lists its K chosen
+ *           experts by selection score descending; equal scores go to the lower
+ *           expert index first.  weights[r][k] belongs to ids[r][k].
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).  Work
+ *           is only enqueued; nothing is synchronised, allocated or freed.
+ * Threads.  Entry points are reentrant and keep no state between calls.
+ * Errors.   Arguments are checked on the host before any HIP call:
+ *             ROUTE_EINVAL   the arguments do not define a routing problem
+ *                            (null pointer with num_tokens > 0, num_tokens < 0,
+ *                            top_k outside [1, topk_group * E / G],
+ *                            E % num_expert_group != 0, topk_group outside
+ *                            [1, num_expert_group], a top-2 group score with
+ *                            groups of one expert, a misaligned pointer, an
+ *                            unknown enum value);
+ *             ROUTE_ENOTSUP  a valid problem outside the compiled range
+ *                            (num_experts > 1024, top_k > 64,
+ *                            num_expert_group > 64; fused router limits below);
+ *             ROUTE_ELAUNCH  the kernel launch failed (hipGetLastError).
+ *           num_tokens == 0 returns ROUTE_OK without touching the GPU.  After an
+ *           error the output contents are unspecified.
+ * Inputs.   Logits (and bias) are expected finite; results for NaN or infinite
+ *           inputs are unspecified.
+ * Precision. Scores are computed in fp32 with the GPU's exp2 and reciprocal
+ *           instructions.  Expert choices therefore agree with an exact
+ *           computation except where two selection scores lie within a few
+ *           fp32 rounding units (a few 1e-7) of each other.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ROUTE_OK = 0,
+    ROUTE_EINVAL = 1,
+    ROUTE_ENOTSUP = 2,
+    ROUTE_ELAUNCH = 3
+} route_status_t;
+
+/* Element type of the router logits / hidden states. */
+typedef enum {
+    ROUTE_F32 = 0,  /* IEEE binary32 */
+    ROUTE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} route_dtype_t;
+
+/* Scoring function.
+ *   ROUTE_SOFTMAX: exp(x_i - max_j x_j) / sum_j exp(x_j - max_j x_j) over all E
+ *                  experts of the row ([ROUTING] section 2).
+ *   ROUTE_SIGMOID: 1 / (1 + exp(-x_i)) ([ROUTING] section 4; [AITER]). */
+typedef enum {
+    ROUTE_SOFTMAX = 0,
+    ROUTE_SIGMOID = 1
+} route_scoring_t;
+
+/* Group score used to rank expert groups (groups are contiguous blocks of
+ * E / num_expert_group experts).
+ *   ROUTE_GROUP_MAX:      the group's largest selection score
+ *                         ([ROUTING] section 3, DeepSeek-V2 style).
+ *   ROUTE_GROUP_TOP2_SUM: the sum of the group's two largest selection scores
+ *                         ([ROUTING] section 4, DeepSeek-V3 style). */
+typedef enum {
+    ROUTE_GROUP_MAX = 0,
+    ROUTE_GROUP_TOP2_SUM = 1
+} route_group_score_t;
+
+/*
+ * Softmax top-k ([ROUTING] section 2): softmax over all E experts, the top_k
+ * largest probabilities and their ids; with renormalize != 0 the K weights are
+ * divided by their sum so they add up to 1.
+ *   gating_output  [num_tokens, num_experts] logits of type `dtype`.
+ */
+route_status_t route_topk_softmax(const void* gating_output, route_dtype_t dtype,
+                                  int64_t num_tokens, int32_t num_experts, int32_t top_k,
+                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
+                                  void* stream);
+
+/*
+ * Grouped top-k ([ROUTING] section 3): score with `scoring_func`, rank the
+ * num_expert_group groups by their largest score (ROUTE_GROUP_MAX), keep the
+ * best topk_group groups (ties: lower group index), then take the top_k
+ * experts of the kept groups.  Weights are the scores of the chosen experts
+ * (for softmax: the probability over all E experts), optionally renormalised.
+ * num_expert_group == 1 is plain top-k.
+ */
+route_status_t route_grouped_topk(const void* gating_output, route_dtype_t dtype,
+                                  int64_t num_tokens, int32_t num_experts, int32_t top_k,
+                                  int32_t num_expert_group, int32_t topk_group,
+                                  int32_t renormalize, route_scoring_t scoring_func,
+                                  float* topk_weights, int32_t* topk_ids, void* stream);
+
+/*
+ * Biased grouped top-k ([ROUTING] section 4; [AITER] "Code analysis"):
+ * s_i = sigmoid(x_i); selection score c_i = s_i + correction_bias[i]; group
+ * score = sum of the group's two largest c (ROUTE_GROUP_TOP2_SUM); keep the
+ * best topk_group groups; take the top_k experts of the kept groups by c.  The
+ * emitted weight is the UNBIASED s of each chosen expert, optionally divided
+ * by the sum of the K weights.  num_expert_group == topk_group == 1 is the
+ * sigmoid-with-bias top-k the [AITER] page swaps in.
+ *   correction_bias  [num_experts] float32, or NULL for all zeros.
+ *   With num_expert_group > 1 every group needs at least two experts.
+ */
+route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_t dtype,
+                                         const float* correction_bias, int64_t num_tokens,
+                                         int32_t num_experts, int32_t top_k,
+                                         int32_t num_expert_group, int32_t topk_group,
+                                         int32_t renormalize, float* topk_weights,
+                                         int32_t* topk_ids, void* stream);
+
+/*
+ * Fused router ([ROUTING] section 5): the router projection
+ *   logits[m][e] = sum_h hidden_states[m][h] * router_weight[h][e]
+ * with bf16 operands and fp32 accumulation, followed in the same kernel by the
+ * routing above (scoring_func, optional correction_bias, group_score rule,
+ * num_expert_group / topk_group, top_k, renormalize).  The logits are never
+ * written to memory.
+ *   hidden_states  [num_tokens, hidden_dim] bf16
+ *   router_weight  [hidden_dim, num_experts] bf16 (expert index contiguous)
+ *   correction_bias [num_experts] float32 or NULL (zeros)
+ * Compiled range: num_experts == 256, hidden_dim a positive multiple of 64,
+ * hidden_states and router_weight 16-byte aligned; other valid shapes return
+ * ROUTE_ENOTSUP.
+ */
+route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
+                                  int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
+                                  route_scoring_t scoring_func, const float* correction_bias,
+                                  route_group_score_t group_score, int32_t top_k,
+                                  int32_t num_expert_group, int32_t topk_group,
+                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
+                                  void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* route_status_str(route_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

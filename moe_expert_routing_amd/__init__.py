@@ -1,0 +1,192 @@
+"""MI355X-native MoE routing top-k: thin Python binding over libmoe_route.so.
+
+Every function here only marshals arguments (torch tensors -> device
+pointers, the current HIP stream) and calls the C-ABI entry point of the same
+name declared in ``include/moe_route.h``.  All routing arithmetic runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback.  If the library
+is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
+
+ROUTE_OK, ROUTE_EINVAL, ROUTE_ENOTSUP, ROUTE_ELAUNCH = 0, 1, 2, 3
+ROUTE_F32, ROUTE_BF16 = 0, 1
+ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
+ROUTE_GROUP_MAX, ROUTE_GROUP_TOP2_SUM = 0, 1
+
+EXPORTED = (
+    "route_topk_softmax",
+    "route_grouped_topk",
+    "route_biased_grouped_topk",
+    "route_fused_router",
+    "route_status_str",
+)
+
+_lib = None
+
+
+class RouteError(RuntimeError):
+    """A kernel launch failed (ROUTE_ELAUNCH)."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types set (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m moe_expert_routing_amd.build` "
+            "(the routing path has no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.route_topk_softmax.argtypes = [p, i32, i64, i32, i32, i32, p, p, p]
+    L.route_grouped_topk.argtypes = [p, i32, i64, i32, i32, i32, i32, i32, i32, p, p, p]
+    L.route_biased_grouped_topk.argtypes = [p, i32, p, i64, i32, i32, i32, i32, i32, p, p, p]
+    L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32, p, p,
+                                     p]
+    for name in EXPORTED[:-1]:
+        getattr(L, name).restype = i32
+    L.route_status_str.argtypes = [i32]
+    L.route_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().route_status_str(code).decode()
+
+
+def _check(code: int, what: str):
+    if code == ROUTE_OK:
+        return
+    msg = f"{what}: {status_str(code)}"
+    if code in (ROUTE_EINVAL, ROUTE_ENOTSUP):
+        raise ValueError(msg)
+    raise RouteError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ROUTE_F32
+    if t.dtype == torch.bfloat16:
+        return ROUTE_BF16
+    raise ValueError(f"router logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _outputs(M, K, device, topk_weights, topk_ids):
+    if topk_weights is None:
+        topk_weights = torch.empty((M, K), dtype=torch.float32, device=device)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, K), dtype=torch.int32, device=device)
+    if topk_weights.dtype != torch.float32 or topk_ids.dtype != torch.int32:
+        raise ValueError("topk_weights must be float32 and topk_ids int32")
+    if tuple(topk_weights.shape) != (M, K) or tuple(topk_ids.shape) != (M, K):
+        raise ValueError(f"outputs must have shape ({M}, {K})")
+    return topk_weights, topk_ids
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scoring_code(scoring_func) -> int:
+    codes = {"softmax": ROUTE_SOFTMAX, "sigmoid": ROUTE_SIGMOID}
+    if scoring_func not in codes:
+        raise ValueError(f"Invalid scoring function: {scoring_func}")
+    return codes[scoring_func]
+
+
+def route_topk_softmax(gating_output, top_k, renormalize=False, topk_weights=None, topk_ids=None,
+                       stream=None):
+    """Softmax top-k over [M, E] logits; returns (topk_weights f32, topk_ids i32)."""
+    M, E = gating_output.shape
+    w, ids = _outputs(M, top_k, gating_output.device, topk_weights, topk_ids)
+    _need_device(gating_output, w, ids)
+    _check(lib().route_topk_softmax(_ptr(gating_output), _dtype_code(gating_output), M, E, top_k,
+                                    int(bool(renormalize)), _ptr(w), _ptr(ids),
+                                    _stream(gating_output.device, stream)),
+           "route_topk_softmax")
+    return w, ids
+
+
+def route_grouped_topk(gating_output, top_k, num_expert_group, topk_group, renormalize=False,
+                       scoring_func="softmax", topk_weights=None, topk_ids=None, stream=None):
+    """Grouped top-k with the per-group max as group score."""
+    M, E = gating_output.shape
+    w, ids = _outputs(M, top_k, gating_output.device, topk_weights, topk_ids)
+    _need_device(gating_output, w, ids)
+    _check(lib().route_grouped_topk(_ptr(gating_output), _dtype_code(gating_output), M, E, top_k,
+                                    num_expert_group, topk_group, int(bool(renormalize)),
+                                    _scoring_code(scoring_func), _ptr(w), _ptr(ids),
+                                    _stream(gating_output.device, stream)),
+           "route_grouped_topk")
+    return w, ids
+
+
+def route_biased_grouped_topk(gating_output, correction_bias, top_k, num_expert_group=1,
+                              topk_group=1, renormalize=False, topk_weights=None, topk_ids=None,
+                              stream=None):
+    """Sigmoid + correction bias, top-2-sum group score; weights are unbiased."""
+    M, E = gating_output.shape
+    w, ids = _outputs(M, top_k, gating_output.device, topk_weights, topk_ids)
+    if correction_bias is not None:
+        if correction_bias.dtype != torch.float32 or tuple(correction_bias.shape) != (E,):
+            raise ValueError("correction_bias must be float32 of shape [E]")
+    _need_device(gating_output, correction_bias, w, ids)
+    _check(lib().route_biased_grouped_topk(_ptr(gating_output), _dtype_code(gating_output),
+                                           _ptr(correction_bias), M, E, top_k, num_expert_group,
+                                           topk_group, int(bool(renormalize)), _ptr(w), _ptr(ids),
+                                           _stream(gating_output.device, stream)),
+           "route_biased_grouped_topk")
+    return w, ids
+
+
+def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, topk_group=1,
+                       renormalize=False, scoring_func="sigmoid", correction_bias=None,
+                       group_score="top2sum", topk_weights=None, topk_ids=None, stream=None):
+    """bf16 router projection [M,H] x [H,E] fused with routing (logits never stored)."""
+    M, H = hidden_states.shape
+    H2, E = router_weight.shape
+    if H2 != H:
+        raise ValueError("hidden_states and router_weight disagree on the hidden size")
+    if hidden_states.dtype != torch.bfloat16 or router_weight.dtype != torch.bfloat16:
+        raise ValueError("fused router operands must be bfloat16")
+    rules = {"max": ROUTE_GROUP_MAX, "top2sum": ROUTE_GROUP_TOP2_SUM}
+    if group_score not in rules:
+        raise ValueError(f"unknown group score {group_score!r}")
+    if correction_bias is not None:
+        if correction_bias.dtype != torch.float32 or tuple(correction_bias.shape) != (E,):
+            raise ValueError("correction_bias must be float32 of shape [E]")
+    w, ids = _outputs(M, top_k, hidden_states.device, topk_weights, topk_ids)
+    _need_device(hidden_states, router_weight, correction_bias, w, ids)
+    _check(lib().route_fused_router(_ptr(hidden_states), _ptr(router_weight), M, H, E,
+                                    _scoring_code(scoring_func), _ptr(correction_bias),
+                                    rules[group_score], top_k, num_expert_group, topk_group,
+                                    int(bool(renormalize)), _ptr(w), _ptr(ids),
+                                    _stream(hidden_states.device, stream)),
+           "route_fused_router")
+    return w, ids

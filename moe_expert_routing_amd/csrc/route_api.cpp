@@ -1,0 +1,119 @@
+// C-ABI entry points: host-side argument validation and dispatch.  No HIP call
+// is made before the arguments are known to define a routing problem.
+#include <stdint.h>
+
+#include "route_internal.h"
+
+using moe_route::FusedProblem;
+using moe_route::RouteProblem;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape rules shared by every routing entry point.  The top-K has to fit in
+// the kept groups; a top-2 group score needs two experts per group.
+route_status_t check_shape(int64_t M, int E, int K, int G, int TG, route_group_score_t rule) {
+    if (M < 0 || E < 1 || G < 1 || E % G != 0) return ROUTE_EINVAL;
+    if (TG < 1 || TG > G) return ROUTE_EINVAL;
+    if (K < 1 || (int64_t)K > (int64_t)TG * (E / G)) return ROUTE_EINVAL;
+    if (rule != ROUTE_GROUP_MAX && rule != ROUTE_GROUP_TOP2_SUM) return ROUTE_EINVAL;
+    if (G > 1 && rule == ROUTE_GROUP_TOP2_SUM && E / G < 2) return ROUTE_EINVAL;
+    if (E > moe_route::kMaxExperts || K > moe_route::kMaxTopK || G > moe_route::kMaxGroups)
+        return ROUTE_ENOTSUP;
+    return ROUTE_OK;
+}
+
+route_status_t check_io(const void* logits, route_dtype_t dtype, const float* bias, int64_t M,
+                        float* w, int32_t* ids) {
+    if (dtype != ROUTE_F32 && dtype != ROUTE_BF16) return ROUTE_EINVAL;
+    if (M == 0) return ROUTE_OK;
+    if (!logits || !w || !ids) return ROUTE_EINVAL;
+    if (!aligned(logits, dtype == ROUTE_F32 ? 4 : 2) || !aligned(w, 4) || !aligned(ids, 4))
+        return ROUTE_EINVAL;
+    if (bias && !aligned(bias, 4)) return ROUTE_EINVAL;
+    return ROUTE_OK;
+}
+
+route_status_t route_common(RouteProblem p) {
+    route_status_t st = check_shape(p.M, p.E, p.K, p.G, p.TG, p.rule);
+    if (st != ROUTE_OK) return st;
+    if (p.scoring != ROUTE_SOFTMAX && p.scoring != ROUTE_SIGMOID) return ROUTE_EINVAL;
+    st = check_io(p.logits, p.dtype, p.bias, p.M, p.weights, p.ids);
+    if (st != ROUTE_OK || p.M == 0) return st;
+    return moe_route::launch_route(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+route_status_t route_topk_softmax(const void* gating_output, route_dtype_t dtype,
+                                  int64_t num_tokens, int32_t num_experts, int32_t top_k,
+                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
+                                  void* stream) {
+    RouteProblem p{gating_output, dtype, nullptr, num_tokens, num_experts, top_k, 1, 1,
+                   ROUTE_SOFTMAX, ROUTE_GROUP_MAX, renormalize != 0, topk_weights, topk_ids,
+                   static_cast<hipStream_t>(stream)};
+    return route_common(p);
+}
+
+route_status_t route_grouped_topk(const void* gating_output, route_dtype_t dtype,
+                                  int64_t num_tokens, int32_t num_experts, int32_t top_k,
+                                  int32_t num_expert_group, int32_t topk_group,
+                                  int32_t renormalize, route_scoring_t scoring_func,
+                                  float* topk_weights, int32_t* topk_ids, void* stream) {
+    RouteProblem p{gating_output, dtype, nullptr, num_tokens, num_experts, top_k,
+                   num_expert_group, topk_group, scoring_func, ROUTE_GROUP_MAX,
+                   renormalize != 0, topk_weights, topk_ids, static_cast<hipStream_t>(stream)};
+    return route_common(p);
+}
+
+route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_t dtype,
+                                         const float* correction_bias, int64_t num_tokens,
+                                         int32_t num_experts, int32_t top_k,
+                                         int32_t num_expert_group, int32_t topk_group,
+                                         int32_t renormalize, float* topk_weights,
+                                         int32_t* topk_ids, void* stream) {
+    RouteProblem p{gating_output, dtype, correction_bias, num_tokens, num_experts, top_k,
+                   num_expert_group, topk_group, ROUTE_SIGMOID, ROUTE_GROUP_TOP2_SUM,
+                   renormalize != 0, topk_weights, topk_ids, static_cast<hipStream_t>(stream)};
+    return route_common(p);
+}
+
+route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
+                                  int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
+                                  route_scoring_t scoring_func, const float* correction_bias,
+                                  route_group_score_t group_score, int32_t top_k,
+                                  int32_t num_expert_group, int32_t topk_group,
+                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
+                                  void* stream) {
+    route_status_t st = check_shape(num_tokens, num_experts, top_k, num_expert_group, topk_group,
+                                    group_score);
+    if (st != ROUTE_OK) return st;
+    if (scoring_func != ROUTE_SOFTMAX && scoring_func != ROUTE_SIGMOID) return ROUTE_EINVAL;
+    if (hidden_dim < 1) return ROUTE_EINVAL;
+    st = check_io(hidden_states, ROUTE_BF16, correction_bias, num_tokens, topk_weights, topk_ids);
+    if (st != ROUTE_OK) return st;
+    if (num_tokens > 0 && (!router_weight || !aligned(router_weight, 2))) return ROUTE_EINVAL;
+    FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim,
+                   RouteProblem{nullptr, ROUTE_BF16, correction_bias, num_tokens, num_experts,
+                                top_k, num_expert_group, topk_group, scoring_func, group_score,
+                                renormalize != 0, topk_weights, topk_ids,
+                                static_cast<hipStream_t>(stream)}};
+    if (!moe_route::fused_router_supported(f)) return ROUTE_ENOTSUP;
+    if (num_tokens == 0) return ROUTE_OK;
+    return moe_route::launch_fused_router(f);
+}
+
+const char* route_status_str(route_status_t status) {
+    switch (status) {
+        case ROUTE_OK: return "ROUTE_OK";
+        case ROUTE_EINVAL: return "ROUTE_EINVAL: invalid argument";
+        case ROUTE_ENOTSUP: return "ROUTE_ENOTSUP: shape outside the compiled range";
+        case ROUTE_ELAUNCH: return "ROUTE_ELAUNCH: kernel launch failed";
+    }
+    return "unknown route_status_t";
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+"""Row-by-row comparison of routing outputs against the oracle.
+
+Rule (the tolerance the benchmark spec states for this path):
+  * ids must equal the oracle's ordered K-vector exactly and every weight must
+    be within 1e-5 absolute;
+  * a row whose oracle scores hold a near tie (a gap below 1e-6 at the K
+    boundary, between consecutive picks, or at the group boundary) may
+    resolve that tie differently, because fp32 scores only approximate the
+    oracle's double values there.  Such a row is accepted only if its output
+    is a valid routing for scores perturbed by at most 1e-6 (checked below),
+    with weights within 1e-5 of the oracle's scores for the ids it chose.
+    These rows are counted by class and reported.
+Anything else is a failure.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import oracle
+
+W_TOL = 1e-5
+TIE = 1e-6
+
+
+@dataclasses.dataclass
+class ParityReport:
+    rows: int = 0
+    exact: int = 0
+    near_tie_k: int = 0
+    near_tie_order: int = 0
+    near_tie_group: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+
+    @property
+    def near_tie(self):
+        return self.near_tie_k + self.near_tie_order + self.near_tie_group
+
+    def ok(self):
+        return not self.failures
+
+    def summary(self):
+        return (f"rows={self.rows} exact={self.exact} near_tie(K={self.near_tie_k}, "
+                f"order={self.near_tie_order}, group={self.near_tie_group}) "
+                f"failures={len(self.failures)} {self.failures[:3]}")
+
+
+def _valid_within(row_logits, ids, w, *, scoring, bias, G, TG, rule, K, renorm):
+    """Is (ids, w) a correct routing of this row once selection scores (and so
+    group scores) may move by up to TIE?  Returns '' when valid, else why not."""
+    s, c = oracle.row_scores(row_logits, scoring=scoring, bias=bias)
+    E = c.shape[0]
+    gs = E // G
+    ids = [int(i) for i in ids]
+    if len(set(ids)) != K or min(ids) < 0 or max(ids) >= E:
+        return "ids are not K distinct experts"
+    if G > 1:
+        h = oracle.group_scores(c, G, rule)
+        used = {i // gs for i in ids}
+        if len(used) > TG:
+            return "ids span more than topk_group groups"
+        rest = sorted((g for g in range(G) if g not in used), key=lambda g: (-h[g], g))
+        kept = used | set(rest[:TG - len(used)])
+        dropped = [h[g] for g in range(G) if g not in kept]
+        if dropped and min(h[g] for g in kept) < max(dropped) - TIE:
+            return "a dropped group beats a kept group by more than the tie window"
+    else:
+        kept = {0}
+    for a, b in zip(ids, ids[1:]):
+        if c[a] < c[b] - TIE:
+            return "picks out of order by more than the tie window"
+    weakest = min(c[i] for i in ids)
+    for j in range(E):
+        if (j // gs) in kept and j not in ids and c[j] > weakest + TIE:
+            return "an unpicked candidate beats a pick by more than the tie window"
+    ws = s[ids]
+    if renorm:
+        ws = ws / ws.sum()
+    if np.max(np.abs(ws - np.asarray(w, np.float64))) > W_TOL:
+        return "weights differ from the oracle scores of the chosen ids"
+    return ""
+
+
+def compare(logits, w_gpu, ids_gpu, *, scoring, bias=None, G=1, TG=1, rule=oracle.GROUP_MAX,
+            K, renorm, oracle_out=None, rows=None):
+    """Compare GPU outputs with the oracle on every row (or the given rows)."""
+    logits = np.asarray(logits)
+    w_gpu = np.asarray(w_gpu)
+    ids_gpu = np.asarray(ids_gpu)
+    if rows is not None:
+        rows = np.asarray(rows)
+        logits, w_gpu, ids_gpu = logits[rows], w_gpu[rows], ids_gpu[rows]
+    if oracle_out is None:
+        oracle_out = oracle.route(logits, K, scoring=scoring, bias=bias, num_expert_group=G,
+                                  topk_group=TG, group_rule=rule, renormalize=renorm,
+                                  with_gaps=True)
+    w_o, ids_o, gaps = oracle_out
+    rep = ParityReport(rows=logits.shape[0])
+    same = np.all(ids_gpu == ids_o, axis=1)
+    close = np.max(np.abs(w_gpu.astype(np.float64) - w_o.astype(np.float64)), axis=1) <= W_TOL
+    good = same & close
+    rep.exact = int(good.sum())
+    for m in np.nonzero(~good)[0]:
+        kgap, ogap, ggap = gaps[m]
+        near = min(kgap, ogap, ggap) < TIE
+        if not near:
+            rep.failures.append((int(m if rows is None else rows[m]), ids_gpu[m].tolist(),
+                                 ids_o[m].tolist(), float(np.max(np.abs(w_gpu[m] - w_o[m])))))
+            continue
+        why = _valid_within(logits[m], ids_gpu[m], w_gpu[m], scoring=scoring, bias=bias, G=G,
+                            TG=TG, rule=rule, K=K, renorm=renorm)
+        if why:
+            rep.failures.append((int(m if rows is None else rows[m]), why, ids_gpu[m].tolist(),
+                                 ids_o[m].tolist()))
+        elif ggap < TIE:
+            rep.near_tie_group += 1
+        elif kgap < TIE:
+            rep.near_tie_k += 1
+        else:
+            rep.near_tie_order += 1
+    return rep

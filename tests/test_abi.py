@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_routing_amd as mr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+# Fake, suitably aligned device addresses: validation never dereferences them.
+# Every call below is rejected, or has num_tokens == 0, so none reaches a HIP
+# call; never add a call here with valid arguments and num_tokens > 0.
+P = ctypes.c_void_p(0x10000)
+Q = ctypes.c_void_p(0x20000)
+R = ctypes.c_void_p(0x30000)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(route_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(mr.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mr.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert mr.status_str(mr.ROUTE_OK) == "ROUTE_OK"
+    assert "invalid" in mr.status_str(mr.ROUTE_EINVAL)
+    assert "compiled range" in mr.status_str(mr.ROUTE_ENOTSUP)
+    assert "launch" in mr.status_str(mr.ROUTE_ELAUNCH)
+    assert mr.status_str(99).startswith("unknown")
+
+
+def bgt(M=4, E=256, K=8, G=8, TG=4, logits=P, dtype=mr.ROUTE_BF16, bias=R, w=Q, ids=R):
+    return mr.lib().route_biased_grouped_topk(logits, dtype, bias, M, E, K, G, TG, 1, w, ids, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), mr.ROUTE_EINVAL),
+    (dict(E=0), mr.ROUTE_EINVAL),
+    (dict(K=0), mr.ROUTE_EINVAL),
+    (dict(G=3), mr.ROUTE_EINVAL),                 # 256 % 3 != 0
+    (dict(TG=0), mr.ROUTE_EINVAL),
+    (dict(TG=9), mr.ROUTE_EINVAL),                # TG > G
+    (dict(K=129), mr.ROUTE_EINVAL),               # K > TG * E/G = 128
+    (dict(E=8, G=8, TG=4, K=2), mr.ROUTE_EINVAL),  # top-2 sum needs 2 experts per group
+    (dict(logits=NULL), mr.ROUTE_EINVAL),
+    (dict(w=NULL), mr.ROUTE_EINVAL),
+    (dict(ids=NULL), mr.ROUTE_EINVAL),
+    (dict(logits=ctypes.c_void_p(0x10001)), mr.ROUTE_EINVAL),  # misaligned bf16
+    (dict(w=ctypes.c_void_p(0x20002)), mr.ROUTE_EINVAL),
+    (dict(bias=ctypes.c_void_p(0x30001)), mr.ROUTE_EINVAL),
+    (dict(dtype=7), mr.ROUTE_EINVAL),
+    (dict(E=2048, G=8, TG=4, K=8), mr.ROUTE_ENOTSUP),          # E beyond 1024
+    (dict(E=256, G=1, TG=1, K=65), mr.ROUTE_ENOTSUP),          # K beyond 64
+    (dict(E=256, G=128, TG=4, K=8), mr.ROUTE_ENOTSUP),         # G beyond 64
+    (dict(M=0, logits=NULL, w=NULL, ids=NULL), mr.ROUTE_OK),   # empty: no launch
+])
+def test_biased_grouped_validation(kw, code):
+    assert bgt(**kw) == code
+
+
+def test_softmax_and_grouped_validation():
+    L = mr.lib()
+    assert L.route_topk_softmax(P, mr.ROUTE_F32, 10, 8, 9, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert L.route_topk_softmax(P, mr.ROUTE_F32, 0, 8, 2, 1, Q, R, None) == mr.ROUTE_OK
+    assert L.route_topk_softmax(NULL, mr.ROUTE_F32, 0, 8, 2, 1, NULL, NULL, None) == mr.ROUTE_OK
+    assert L.route_topk_softmax(ctypes.c_void_p(0x10002), mr.ROUTE_F32, 5, 8, 2, 1, Q, R,
+                                None) == mr.ROUTE_EINVAL
+    # scoring enum
+    assert L.route_grouped_topk(P, mr.ROUTE_F32, 5, 160, 6, 8, 3, 0, 5, Q, R, None) == \
+        mr.ROUTE_EINVAL
+    # grouped with the max rule accepts groups of one expert
+    assert L.route_grouped_topk(P, mr.ROUTE_F32, 0, 8, 2, 8, 4, 0, mr.ROUTE_SOFTMAX, Q, R,
+                                None) == mr.ROUTE_OK
+    assert L.route_grouped_topk(P, mr.ROUTE_F32, 5, 160, 61, 8, 3, 0, mr.ROUTE_SOFTMAX, Q, R,
+                                None) == mr.ROUTE_EINVAL
+
+
+def test_fused_router_validation():
+    L = mr.lib()
+    f = L.route_fused_router
+    sig, top2 = mr.ROUTE_SIGMOID, mr.ROUTE_GROUP_TOP2_SUM
+    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    # outside the compiled range
+    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_ENOTSUP
+    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_ENOTSUP
+    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, NULL, NULL, None) == \
+        mr.ROUTE_OK
+
+
+def test_binding_has_no_cpu_fallback():
+    import torch
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        mr.route_topk_softmax(x, 2)
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        mr.route_biased_grouped_topk(x.bfloat16(), torch.zeros(8), 2, 2, 1)

@@ -1,0 +1,146 @@
+"""GPU parity: every routing entry point against the CPU oracle on the same
+seeded inputs (full workload sizes, an M sweep, random shapes with ragged
+tails, ties, edge cases)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_routing_amd as mr
+from gpu_util import log, oracle_args, route_gpu, to_device
+from parity_check import compare
+from workloads import (BIASED_GROUPED_M_SWEEP, WORKLOADS, bf16_bits_from_f32, make_bias,
+                       make_logits, random_logits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_workload(wl, M=None):
+    x = make_logits(wl, M)
+    b = make_bias(wl)
+    log(f"[gpu] {wl.entry} workload={wl.name} M={x.shape[0]} E={wl.E} K={wl.K} G={wl.G} "
+        f"TG={wl.TG}")
+    w, ids = route_gpu(wl.entry, to_device(x), K=wl.K, G=wl.G, TG=wl.TG, scoring=wl.scoring,
+                       bias=None if b is None else to_device(b), renorm=wl.renormalize)
+    sc, rule = oracle_args(wl.entry, wl.scoring)
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=wl.G, TG=wl.TG, rule=rule, K=wl.K,
+                  renorm=wl.renormalize)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+    # near ties must stay rare: they come only from sub-1e-6 gaps
+    assert rep.near_tie <= max(2, rep.rows // 1000), rep.summary()
+    return rep
+
+
+@pytest.mark.parametrize("name", ["softmax_e8_k2", "sigmoid_bias_e256_k8", "grouped_softmax_e160"])
+def test_workload_full_size(name):
+    _check_workload(WORKLOADS[name])
+
+
+@pytest.mark.parametrize("M", BIASED_GROUPED_M_SWEEP)
+def test_biased_grouped_m_sweep(M):
+    _check_workload(WORKLOADS["biased_grouped_e256"], M)
+
+
+def _random_cases():
+    cases = []
+    rng = np.random.default_rng(2024)
+    shapes = [(8, 1), (8, 2), (16, 4), (60, 1), (60, 6), (64, 8), (128, 8), (160, 8), (160, 1),
+              (192, 6), (256, 1), (256, 8), (256, 16), (384, 8), (512, 16), (1024, 32), (100, 5),
+              (72, 9), (256, 64), (48, 3)]
+    entries = ["route_topk_softmax", "route_grouped_topk", "route_biased_grouped_topk"]
+    for i, (E, G) in enumerate(shapes):
+        for entry in entries:
+            if entry == "route_topk_softmax" and G != 1:
+                continue
+            if entry == "route_biased_grouped_topk" and G > 1 and E // G < 2:
+                continue
+            TG = int(rng.integers(1, G + 1))
+            K = int(rng.integers(1, min(TG * (E // G), 64) + 1))
+            dtype = ["f32", "bf16"][(i + len(cases)) % 2]
+            scoring = "softmax" if entry == "route_topk_softmax" else \
+                ["softmax", "sigmoid"][len(cases) % 2]
+            M = int(rng.choice([1, 3, 63, 65, 257, 1000]))
+            cases.append((entry, E, G, TG, K, dtype, scoring, bool(len(cases) % 2), M,
+                          int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("entry,E,G,TG,K,dtype,scoring,renorm,M,seed", _random_cases())
+def test_random_shapes(entry, E, G, TG, K, dtype, scoring, renorm, M, seed):
+    rng = np.random.default_rng(seed)
+    x = random_logits(rng, M, E, dtype, std=1.5)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32) \
+        if entry == "route_biased_grouped_topk" and seed % 3 else None
+    log(f"[gpu] {entry} E={E} G={G} TG={TG} K={K} {dtype} {scoring} renorm={renorm} M={M} "
+        f"seed={seed}")
+    w, ids = route_gpu(entry, to_device(x), K=K, G=G, TG=TG, scoring=scoring,
+                       bias=None if b is None else to_device(b), renorm=renorm)
+    sc, rule = oracle_args(entry, scoring)
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=G, TG=TG, rule=rule, K=K, renorm=renorm)
+    assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("entry,scoring", [("route_biased_grouped_topk", "sigmoid"),
+                                           ("route_grouped_topk", "softmax"),
+                                           ("route_topk_softmax", "softmax")])
+def test_exact_ties_resolve_by_index(entry, scoring):
+    """Logits drawn from 5 values: most scores tie exactly and the lower
+    expert index must win, with no tolerance."""
+    rng = np.random.default_rng(77)
+    M, E = 512, 256
+    G, TG, K = (1, 1, 8) if entry == "route_topk_softmax" else (8, 4, 8)
+    x = bf16_bits_from_f32((rng.integers(-2, 3, size=(M, E)) * 0.5).astype(np.float32))
+    log(f"[gpu] ties {entry} M={M} E={E}")
+    w, ids = route_gpu(entry, to_device(x), K=K, G=G, TG=TG, scoring=scoring, renorm=True)
+    sc, rule = oracle_args(entry, scoring)
+    rep = compare(x, w, ids, scoring=sc, G=G, TG=TG, rule=rule, K=K, renorm=True)
+    assert rep.ok() and rep.exact == M, rep.summary()
+
+
+def test_empty_batch():
+    wl = WORKLOADS["biased_grouped_e256"]
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    b = to_device(make_bias(wl))
+    w, ids = mr.route_biased_grouped_topk(x, b, 8, 8, 4, True)
+    torch.cuda.synchronize()
+    assert w.shape == (0, 8) and ids.shape == (0, 8)
+
+
+def test_k_equals_all_candidates():
+    rng = np.random.default_rng(3)
+    x = random_logits(rng, 33, 64, "f32")
+    log("[gpu] K = TG*E/G")
+    w, ids = route_gpu("route_grouped_topk", to_device(x), K=16, G=8, TG=2, scoring="sigmoid",
+                       renorm=True)
+    rep = compare(x, w, ids, scoring=1, G=8, TG=2, rule=0, K=16, renorm=True)
+    assert rep.ok(), rep.summary()
+
+
+def test_deterministic_and_stream_and_row_independent():
+    wl = WORKLOADS["biased_grouped_e256"]
+    x = to_device(make_logits(wl, 4099))
+    b = to_device(make_bias(wl))
+    log("[gpu] determinism / side stream / row subsets")
+    w1, i1 = mr.route_biased_grouped_topk(x, b, 8, 8, 4, True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        w2, i2 = mr.route_biased_grouped_topk(x, b, 8, 8, 4, True, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(w1, w2) and torch.equal(i1, i2)
+    w3, i3 = mr.route_biased_grouped_topk(x[1000:1777].contiguous(), b, 8, 8, 4, True)
+    torch.cuda.synchronize()
+    assert torch.equal(w3, w1[1000:1777]) and torch.equal(i3, i1[1000:1777])
+
+
+def test_bad_arguments_raise_before_launch():
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(256, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        mr.route_biased_grouped_topk(x, b, 8, 3, 1, True)      # 256 % 3
+    with pytest.raises(ValueError):
+        mr.route_biased_grouped_topk(x, b, 200, 8, 4, True)    # K > TG*E/G
+    with pytest.raises(ValueError):
+        mr.route_grouped_topk(x, 8, 8, 4, True, scoring_func="tanh")
+    with pytest.raises(ValueError):
+        mr.route_topk_softmax(x.t(), 2)                         # not contiguous
