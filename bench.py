@@ -1,0 +1,242 @@
+"""Benchmark: biased grouped top-k routing on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one call of route_biased_grouped_topk over the whole batch of
+router logits (sigmoid + correction bias, 8 groups of 32 of 256 experts,
+top-4 groups, top-8 experts, renormalised; bf16 logits, M = 65536 tokens).
+Inputs are seeded synthetic data already resident in device memory.  The
+call rotates over several identical input/output sets whose total size is
+far larger than the 256 MB last-level cache, so each call reads its logits
+from HBM.  Prints one JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "routed tokens/s + HBM GB/s at M=64K E=256 K=8; µs/call at M=64"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "biased_grouped_e256"
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M, E, K, logit_bytes, bias=True):
+    """One read of the logits (and the bias), one write of weights + ids."""
+    return M * E * logit_bytes + M * K * 8 + (E * 4 if bias else 0)
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on the same workload."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_bias, make_logits
+
+    x = make_logits(wl)
+    b = make_bias(wl)
+    rows = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.route(x, wl.K, scoring=oracle.SIGMOID, bias=b, num_expert_group=wl.G,
+                     topk_group=wl.TG, group_rule=oracle.GROUP_TOP2SUM,
+                     renormalize=wl.renormalize)
+        rows += x.shape[0]
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full passes over the {x.shape[0]}-token batch "
+                      f"({dt:.1f} s, single-threaded C oracle in double precision)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: routing is per token and needs no collective; "
+              f"--gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_routing_amd as mr
+    from workloads import WORKLOADS, make_bias, make_logits
+
+    wl = WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda", 0)
+    x_np = make_logits(wl)
+    b_np = make_bias(wl)
+    M, E, K = x_np.shape[0], wl.E, wl.K
+    bytes_per_call = algorithmic_bytes(M, E, K, 2)
+    set_bytes = M * E * 2 + M * K * 8
+    sets = args.sets or max(2, -(-1024 * 2**20 // set_bytes))  # >= 1 GiB in rotation
+    x0 = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    bias = torch.from_numpy(b_np).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    ws = [torch.empty((M, K), dtype=torch.float32, device=dev) for _ in range(sets)]
+    ids = [torch.empty((M, K), dtype=torch.int32, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        s = i % sets
+        mr.route_biased_grouped_topk(xs[s], bias, K, wl.G, wl.TG, wl.renormalize,
+                                     topk_weights=ws[s], topk_ids=ids[s], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back calls; events on the launch stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = M / (ms_per_step * 1e-3)
+
+    # per-launch kernel duration: an event pair around each launch
+    n_pair = min(args.steps, 400)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_pair)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    achieved = bytes_per_call / (kern_ms * 1e-3) / 1e9
+
+    # warm (cache-resident) figure for context
+    for i in range(50):
+        mr.route_biased_grouped_topk(x0, bias, K, wl.G, wl.TG, wl.renormalize,
+                                     topk_weights=ws[0], topk_ids=ids[0], stream=stream)
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for i in range(200):
+        mr.route_biased_grouped_topk(x0, bias, K, wl.G, wl.TG, wl.renormalize,
+                                     topk_weights=ws[0], topk_ids=ids[0], stream=stream)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e2.elapsed_time(e3) / 200
+
+    # decode-size latency: M = 64, back-to-back enqueue and HIP-graph replay
+    x64 = x0[:64].contiguous()
+    w64 = torch.empty((64, K), dtype=torch.float32, device=dev)
+    i64 = torch.empty((64, K), dtype=torch.int32, device=dev)
+    for _ in range(100):
+        mr.route_biased_grouped_topk(x64, bias, K, wl.G, wl.TG, wl.renormalize, w64, i64,
+                                     stream=stream)
+    torch.cuda.synchronize()
+    e4, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e4.record(stream)
+    for _ in range(1000):
+        mr.route_biased_grouped_topk(x64, bias, K, wl.G, wl.TG, wl.renormalize, w64, i64,
+                                     stream=stream)
+    e5.record(stream)
+    torch.cuda.synchronize()
+    m64_loop_us = e4.elapsed_time(e5)
+    pairs64 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(200)]
+    for a, b in pairs64:
+        a.record(stream)
+        mr.route_biased_grouped_topk(x64, bias, K, wl.G, wl.TG, wl.renormalize, w64, i64,
+                                     stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    m64_kernel_us = float(np.mean([a.elapsed_time(b) for a, b in pairs64])) * 1e3
+    graph_us = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            mr.route_biased_grouped_topk(x64, bias, K, wl.G, wl.TG, wl.renormalize, w64, i64,
+                                         stream=side)
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(100):
+                    mr.route_biased_grouped_topk(x64, bias, K, wl.G, wl.TG, wl.renormalize,
+                                                 w64, i64, stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e6, e7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e6.record(stream)
+        for _ in range(10):
+            g.replay()
+        e7.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e6.elapsed_time(e7) * 1e3 / 1000
+    except Exception as exc:  # graph capture is optional context
+        eprint(f"[bench] graph replay skipped: {exc}")
+
+    # every set holds the same inputs, so every set must hold identical results
+    for i in range(sets):
+        step(i)
+    torch.cuda.synchronize()
+    for s in range(1, sets):
+        if not (torch.equal(ws[s], ws[0]) and torch.equal(ids[s], ids[0])):
+            raise SystemExit("rotating sets disagree")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "biased grouped top-k routing (DeepSeek-V3 shape)",
+                   "tokens": M, "experts": E, "top_k": K, "num_expert_group": wl.G,
+                   "topk_group": wl.TG, "scoring": "sigmoid+correction_bias",
+                   "group_score": "top-2 sum", "renormalize": wl.renormalize,
+                   "logits": "bf16 N(0, var 2)", "bias": "fp32 N(0, var 0.02)",
+                   "rotating_sets": sets, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+        "hbm_GBps_whole_step": bytes_per_call / (ms_per_step * 1e-3) / 1e9,
+        "kernel_us_event_pairs": kern_ms * 1e3,
+        "warm_cache_us_per_call": warm_ms * 1e3,
+        "M64": {"kernel_us_event_pairs": m64_kernel_us, "loop_us_per_call": m64_loop_us,
+                "graph_us_per_call": graph_us},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
