@@ -1,0 +1,413 @@
+// Device-side routing core shared by the standalone routing kernel and the
+// fused router's epilogue (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "route_common.cuh"
+
+namespace moe_route {
+
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppXor3 = 0x1B;     // quad_perm [3,2,1,0]
+constexpr int kDppMirror8 = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// Reductions over the LPR lanes of a row; every lane of the row gets the
+// same bits (xor/mirror butterflies combine the same operands in each lane).
+template <int LPR>
+__device__ __forceinline__ float row_max(float v) {
+    if (LPR >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    if (LPR >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    if (LPR >= 8) v = fmaxf(v, dpp_f32<kDppMirror8>(v));
+    return v;
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+    if (LPR >= 2) v = v + dpp_f32<kDppXor1>(v);
+    if (LPR >= 4) v = v + dpp_f32<kDppXor2>(v);
+    if (LPR >= 8) v = v + dpp_f32<kDppMirror8>(v);
+    return v;
+}
+template <int LPR>
+__device__ __forceinline__ float row_min(float v) {
+    if (LPR >= 2) v = fminf(v, dpp_f32<kDppXor1>(v));
+    if (LPR >= 4) v = fminf(v, dpp_f32<kDppXor2>(v));
+    if (LPR >= 8) v = fminf(v, dpp_f32<kDppMirror8>(v));
+    return v;
+}
+template <int LPR>
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    if (LPR >= 2) v = max(v, dpp_u32<kDppXor1>(v));
+    if (LPR >= 4) v = max(v, dpp_u32<kDppXor2>(v));
+    if (LPR >= 8) v = max(v, dpp_u32<kDppMirror8>(v));
+    return v;
+}
+// Row argmax over (value desc, index asc) pairs.
+template <int LPR>
+__device__ __forceinline__ void row_argmax(float& v, int& i) {
+#define MOE_ROUTE_ARGMAX_STEP(CTRL)                                   \
+    {                                                                 \
+        float ov = dpp_f32<CTRL>(v);                                  \
+        int oi = static_cast<int>(dpp_u32<CTRL>(static_cast<uint32_t>(i))); \
+        if (beats(ov, oi, v, i)) { v = ov; i = oi; }                  \
+    }
+    if (LPR >= 2) MOE_ROUTE_ARGMAX_STEP(kDppXor1)
+    if (LPR >= 4) MOE_ROUTE_ARGMAX_STEP(kDppXor2)
+    if (LPR >= 8) MOE_ROUTE_ARGMAX_STEP(kDppMirror8)
+#undef MOE_ROUTE_ARGMAX_STEP
+}
+
+// Whole-wave min / max (all lanes hold the result).
+__device__ __forceinline__ float wave_min_all(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fminf(v, shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ float load_one(const T* p, int i);
+template <>
+__device__ __forceinline__ float load_one<float>(const float* p, int i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_one<uint16_t>(const uint16_t* p, int i) {
+    return bf16_bits_to_float(p[i]);
+}
+
+// Median of three (one v_med3_u32).
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+    return max(min(a, b), min(max(a, b), c));
+}
+
+// Insert key k into the descending list L[0..T-1] (keys are unique): the new
+// t-th largest of {L, k} is the median of (L[t-1], L[t], k).
+template <int T>
+__device__ __forceinline__ void list_insert(uint32_t (&L)[T], uint32_t k) {
+#pragma unroll
+    for (int t = T - 1; t >= 1; --t) L[t] = umed3(L[t - 1], L[t], k);
+    L[0] = max(L[0], k);
+}
+
+// Fixed-point key of a selection score: t = (c - lo) * 2^23 / R + 2^23 lies in
+// [2^23, 2^24), so its fp32 mantissa is the fixed-point value; shifting the
+// float bits left by 9 drops the exponent and leaves room for the index.
+__device__ __forceinline__ uint32_t make_key(float c, float scale, float offs, uint32_t low9) {
+    float t = __builtin_fmaf(c, scale, offs);
+    return (__float_as_uint(t) << 9) | low9;
+}
+
+// LDS tile of a wave: RPW rows x E fp32 selection scores, stored in 16-byte
+// chunks.  Logical chunk q of a row lives at physical chunk
+// q ^ ((q >> 3) & 7), a permutation inside each aligned block of 8 chunks.
+// With 8 chunks per lane (E = 256) the 8 lanes of a row, which write the same
+// chunk number in one instruction, land in 8 different bank groups.
+__device__ __forceinline__ int swz_chunk(int q) { return q ^ ((q >> 3) & 7); }
+__device__ __forceinline__ int swz_elem(int e) { return swz_chunk(e >> 2) * 4 + (e & 3); }
+
+struct KeyParams {
+    float scale, offs;
+    bool exact_only;  // the fixed-point step would be too coarse
+};
+
+// Choose the fixed-point window [lo, lo + R) that holds every selection score.
+__device__ __forceinline__ KeyParams key_params(float cmin, float cmax) {
+    float span = (cmax - cmin) * 1.001f + 1e-6f;
+    float R = 2.0f;
+    while (R < span) R *= 2.0f;
+    float lo = cmin - R * (1.0f / 1048576.0f);  // keeps t >= 2^23 + 8
+    KeyParams kp;
+    kp.scale = 8388608.0f / R;
+    kp.offs = 8388608.0f - lo * kp.scale;
+    kp.exact_only = R > 4.0f;
+    return kp;
+}
+
+// Offsets inside a row of the per-wave LDS tile (ROW fp32 values); 16-byte
+// chunks are permuted within aligned blocks of 8 (see swz_chunk) when the row
+// spans whole blocks.
+template <int ROW>
+__device__ __forceinline__ int tile_chunk(int q) {
+    if constexpr ((ROW / 4) % 8 == 0) return swz_chunk(q);
+    return q;
+}
+template <int ROW>
+__device__ __forceinline__ int tile_elem(int i) {
+    return tile_chunk<ROW>(i >> 2) * 4 + (i & 3);
+}
+
+// Unbiased score of a logit: sigmoid, or the softmax numerator exp(x - max).
+template <bool SOFTMAX>
+__device__ __forceinline__ float lane_score(float x, float mx) {
+    if constexpr (SOFTMAX) return fast_exp2((x - mx) * kLog2e);
+    return sigmoid_f32(x);
+}
+
+// Route the rows of one wave tile.  Lane `sub` of row-in-wave `rw` brings the
+// fp32 logits x[0..VPL) of experts [sub*VPL, sub*VPL + VPL) of token `row`
+// (valid == false past the last token: computed, never stored).  my_row is
+// this row's E-float LDS scratch (LPR > 1); s_bias the bias in LDS (BIAS);
+// logit_of(e) returns the fp32 logit of expert e of this row (rare paths).
+// Steps follow "[SGLang] MoE routing: token-to-expert assignment algorithms",
+// sections 2-4; see the file header of route_fast.hip for the design.
+template <int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/, int SPLIT,
+          int TL, int KMAX, typename LogitFn>
+__device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const int rw,
+                                           const bool valid, const int64_t row, float* my_row,
+                                           const float* s_bias, const KeyParams& kp, const int TG,
+                                           const int K, const int renorm, float* __restrict__ w_out,
+                                           int32_t* __restrict__ id_out, LogitFn logit_of) {
+    constexpr int E = LPR * VPL;
+    constexpr int NC = GRP ? VPL / SPLIT : VPL;    // candidates per lane in the list step
+    constexpr int SLOTS = (KMAX + LPR - 1) / LPR;  // output slots per lane
+    constexpr int CPL = VPL / 4;                   // 16-byte chunks per lane
+    constexpr int ROW = LPR > 1 ? E : 4;           // fp32 values per row in LDS
+    static_assert(GRP == 0 || VPL % SPLIT == 0, "a group splits evenly");
+    static_assert(E <= 512, "9 index bits");
+    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
+    static_assert(GRP == 0 || LPR == 8, "grouped kernels hold one of 8 groups per lane");
+    static_assert(TL >= KMAX || TL >= NC, "a lane's list never runs dry");
+    static_assert(VPL % 4 == 0 && SLOTS <= 2, "");
+    // Group scores as fixed point with the key step: (h - lo) * scale for the
+    // max rule, (h - 2 lo) * scale for the top-2 sum; both lie in [0, 2^24).
+    const float h_offs = (GRP == 2 ? 2.0f : 1.0f) * (kp.offs - 8388608.0f);
+
+    // ---- 1. scores s (stored to LDS) and selection scores c = s + bias
+    float mx = 0.f, row_total = 1.f;
+    if constexpr (SOFTMAX) {
+        float m = x[0];
+#pragma unroll
+        for (int j = 1; j < VPL; ++j) m = fmaxf(m, x[j]);
+        mx = row_max<LPR>(m);
+    }
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            x[j] = lane_score<SOFTMAX>(x[j], mx);
+            if constexpr (SOFTMAX) acc += x[j];
+        }
+        if constexpr (SOFTMAX) row_total = row_sum<LPR>(acc);
+    }
+    if constexpr (LPR > 1) {
+#pragma unroll
+        for (int v = 0; v < CPL; ++v)
+            reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v)] =
+                make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int v = 0; v < CPL; ++v) {
+            const float4 d = reinterpret_cast<const float4*>(s_bias + sub * VPL)[v];
+            x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
+        }
+    }
+    // x now holds the selection scores c of the lane's experts
+
+    // ---- 2. group score, rank among the row's 8 groups, keep the best TG
+    uint32_t kept_row = 1u;
+    if constexpr (GRP != 0) {
+        float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+            if (GRP == 2) m2 = __builtin_amdgcn_fmed3f(m1, m2, x[j]);
+            m1 = fmaxf(m1, x[j]);
+        }
+        const float h = GRP == 2 ? m1 + m2 : m1;
+        const uint32_t hq = static_cast<uint32_t>(__builtin_fmaf(h, kp.scale, h_offs));
+        const uint32_t hk = (hq << 3) | static_cast<uint32_t>(7 - sub);
+        uint32_t rank = 0;
+        const uint32_t m7 = dpp_u32<kDppMirror8>(hk);
+        rank += dpp_u32<kDppXor1>(hk) > hk;
+        rank += dpp_u32<kDppXor2>(hk) > hk;
+        rank += dpp_u32<kDppXor3>(hk) > hk;
+        rank += m7 > hk;
+        rank += dpp_u32<kDppXor1>(m7) > hk;
+        rank += dpp_u32<kDppXor2>(m7) > hk;
+        rank += dpp_u32<kDppXor3>(m7) > hk;
+        const uint64_t kept_wave = __ballot(rank < static_cast<uint32_t>(TG));
+        kept_row = static_cast<uint32_t>(kept_wave >> (rw * LPR)) & 0xffu;
+    }
+
+    // ---- 3. candidates -> keys -> sorted list of the lane's TL best keys
+    int cand_base = sub * VPL;  // expert index of this lane's first candidate
+    bool has_cand = true;
+    float cc[NC];
+    if constexpr (GRP != 0) {
+        wave_lds_sync();
+        const int k = sub / SPLIT, part = sub % SPLIT;
+        uint32_t m = kept_row;
+#pragma unroll
+        for (int i = 0; i < LPR / SPLIT - 1; ++i)
+            if (i < k) m &= m - 1u;
+        const int g = m ? __builtin_ctz(m) : 0;
+        has_cand = k < TG && m != 0u;
+        cand_base = g * VPL + part * NC;
+        if constexpr (NC % 4 == 0) {
+#pragma unroll
+            for (int v = 0; v < NC / 4; ++v) {
+                const float4 d = reinterpret_cast<const float4*>(
+                    my_row)[tile_chunk<ROW>((cand_base >> 2) + v)];
+                cc[4 * v] = d.x; cc[4 * v + 1] = d.y; cc[4 * v + 2] = d.z; cc[4 * v + 3] = d.w;
+            }
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int v = 0; v < NC / 4; ++v) {
+                    const float4 d = reinterpret_cast<const float4*>(s_bias + cand_base)[v];
+                    cc[4 * v] += d.x; cc[4 * v + 1] += d.y;
+                    cc[4 * v + 2] += d.z; cc[4 * v + 3] += d.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                cc[j] = my_row[tile_elem<ROW>(cand_base + j)];
+                if constexpr (BIAS) cc[j] += s_bias[cand_base + j];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NC; ++j) cc[j] = x[j];
+    }
+    uint32_t L[TL];
+#pragma unroll
+    for (int t = 0; t < TL; ++t) L[t] = 0u;
+    if (has_cand) {
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            list_insert<TL>(L, make_key(cc[j], kp.scale, kp.offs, (uint32_t)(NC - 1 - j)));
+    }
+    // low 9 bits := 511 - expert index; empty slots stay below 512
+    const uint32_t base9 = 511u - (uint32_t)(cand_base + NC - 1);
+#pragma unroll
+    for (int t = 0; t < TL; ++t) L[t] += base9;
+
+    // ---- 4. merge: K rounds of a row-wide maximum over the list heads
+    uint32_t wk[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) wk[s] = 0u;
+    if constexpr (LPR == 1) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) wk[s] = L[s];
+    } else {
+#pragma unroll 1
+        for (int r = 0; r < K; ++r) {
+            const uint32_t w = row_max_u32<LPR>(L[0]);
+            const bool mine = (L[0] == w);
+#pragma unroll
+            for (int t = 0; t < TL - 1; ++t) L[t] = mine ? L[t + 1] : L[t];
+            L[TL - 1] = mine ? base9 : L[TL - 1];
+            if (sub == r % LPR) {
+                if (SLOTS == 1 || r < LPR) wk[0] = w;
+                else wk[SLOTS - 1] = w;
+            }
+        }
+    }
+    int pick[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) pick[s] = 511 - (int)(wk[s] & 511u);
+
+    // ---- exact path for a bias spread too wide for the key window: K
+    // rounds of a (value, index) argmax on the fp32 selection scores.
+    // Rolled loops and LDS re-reads keep this rare path off the register
+    // budget of the main path.
+    if (kp.exact_only) {
+        auto cval = [&](int e) {  // selection score c of expert e of this row
+            float v = lane_score<SOFTMAX>(logit_of(e), mx);
+            if constexpr (BIAS) v += s_bias[e];
+            return v;
+        };
+        bool kept = true;
+        if constexpr (GRP != 0) {
+            float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll 1
+            for (int j = 0; j < VPL; ++j) {
+                const float c = cval(sub * VPL + j);
+                if (GRP == 2) m2 = __builtin_amdgcn_fmed3f(m1, m2, c);
+                m1 = fmaxf(m1, c);
+            }
+            const float h = GRP == 2 ? m1 + m2 : m1;
+            int rank = 0;
+#pragma unroll 1
+            for (int d = 1; d < LPR; ++d) {
+                const float o = __shfl(h, rw * LPR + (sub ^ d), kWave);
+                rank += beats(o, sub ^ d, h, sub) ? 1 : 0;
+            }
+            kept = rank < TG;
+        }
+        float bv_prev = INFINITY;
+        int bi_prev = -1;
+#pragma unroll 1
+        for (int r = 0; r < K; ++r) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            if (kept) {
+#pragma unroll 1
+                for (int j = 0; j < VPL; ++j) {
+                    const int e = sub * VPL + j;
+                    const float v = cval(e);
+                    if (beats(bv_prev, bi_prev, v, e) && beats(v, e, bv, bi)) { bv = v; bi = e; }
+                }
+            }
+            row_argmax<LPR>(bv, bi);
+            bv_prev = bv;
+            bi_prev = bi;
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s)
+                if (r == s * LPR + sub) pick[s] = bi;
+        }
+    }
+
+    // ---- 5. weights from the unbiased scores, renormalisation, stores
+    if constexpr (LPR > 1 && GRP == 0) wave_lds_sync();
+    float wsl[SLOTS];
+    float part_sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+        const int r = s * LPR + sub;
+        pick[s] = min(max(pick[s], 0), E - 1);  // never read outside the row
+        float sv;
+        if constexpr (LPR > 1) {
+            sv = my_row[tile_elem<ROW>(pick[s])];
+        } else if constexpr (SOFTMAX) {
+            sv = x[0];  // one lane per row: x holds the numerators
+#pragma unroll
+            for (int j = 1; j < VPL; ++j) sv = (pick[s] == j) ? x[j] : sv;
+        } else {
+            // one lane per row: x holds c; recompute s of the pick from its logit
+            sv = valid ? sigmoid_f32(logit_of(pick[s])) : 0.f;
+        }
+        if constexpr (SOFTMAX) sv = sv / row_total;
+        wsl[s] = (r < K) ? sv : 0.f;
+        part_sum += wsl[s];
+    }
+    const float inv_tot = fast_rcp(row_sum<LPR>(part_sum));
+    if (valid) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+            const int r = s * LPR + sub;
+            if (r < K) {
+                w_out[row * K + r] = renorm ? wsl[s] * inv_tot : wsl[s];
+                id_out[row * K + r] = pick[s];
+            }
+        }
+    }
+    if constexpr (LPR > 1) wave_lds_sync();  // the next tile rewrites the LDS rows
+}
+
+}  // namespace moe_route

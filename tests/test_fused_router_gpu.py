@@ -1,0 +1,94 @@
+"""GPU parity of route_fused_router (bf16 router projection on MFMA + routing
+epilogue) against the oracle: the oracle's logits are the exact double
+products summed in double, then routed exactly like the standalone oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_routing_amd as mr
+import oracle
+from gpu_util import log, to_device
+from parity_check import compare
+from workloads import (WORKLOADS, bf16_bits_from_f32, make_bias, make_router_inputs)
+
+pytestmark = pytest.mark.gpu
+
+SC = {"sigmoid": oracle.SIGMOID, "softmax": oracle.SOFTMAX}
+RU = {"top2sum": oracle.GROUP_TOP2SUM, "max": oracle.GROUP_MAX}
+
+
+def _inputs(rng, M, H, E=256, bias=True):
+    hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32))
+    w = bf16_bits_from_f32(rng.standard_normal((H, E), dtype=np.float32) * np.float32(H ** -0.5))
+    b = (rng.standard_normal(E, dtype=np.float32) * np.float32(0.02 ** 0.5)) if bias else None
+    return hidden, w, b
+
+
+def _run(hidden, w, b, K, G, TG, renorm, scoring, rule):
+    wt, ids = mr.route_fused_router(to_device(hidden), to_device(w), K, G, TG, renorm, scoring,
+                                    None if b is None else to_device(b), rule)
+    torch.cuda.synchronize()
+    return wt.cpu().numpy(), ids.cpu().numpy()
+
+
+def _check(hidden, w, b, wt, ids, rows, K, G, TG, renorm, scoring, rule):
+    logits = oracle.router_logits(hidden[rows], w)
+    rep = compare(logits, wt[rows], ids[rows], scoring=SC[scoring], bias=b, G=G, TG=TG,
+                  rule=RU[rule], K=K, renorm=renorm)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+    return rep
+
+
+@pytest.mark.parametrize("M,H,G,TG,K,scoring,rule,bias,renorm", [
+    (77, 128, 8, 4, 8, "sigmoid", "top2sum", True, True),     # ragged last block
+    (32, 64, 8, 4, 8, "sigmoid", "top2sum", True, False),     # one step of K
+    (200, 512, 1, 1, 8, "sigmoid", "top2sum", True, True),    # ungrouped
+    (65, 256, 8, 3, 6, "softmax", "max", False, False),       # softmax, group max
+    (96, 192, 8, 2, 4, "sigmoid", "max", False, True),        # sigmoid, no bias
+    (1, 64, 8, 4, 8, "sigmoid", "top2sum", True, True),       # single token
+])
+def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm):
+    rng = np.random.default_rng(M * 1000 + H)
+    hidden, w, b = _inputs(rng, M, H, bias=bias)
+    log(f"[gpu] route_fused_router M={M} H={H} G={G} TG={TG} K={K} {scoring} {rule} "
+        f"bias={bias}")
+    wt, ids = _run(hidden, w, b, K, G, TG, renorm, scoring, rule)
+    _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, renorm, scoring, rule)
+
+
+def test_fused_router_full_workload_sampled():
+    wl = WORKLOADS["fused_router_h7168"]
+    hidden, w = make_router_inputs(wl)
+    b = make_bias(wl)
+    log(f"[gpu] route_fused_router workload={wl.name} M={wl.M} H={wl.hidden_dim}")
+    wt, ids = _run(hidden, w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
+    # oracle on sampled rows: both ends of the batch, block boundaries, random
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(wl.M - 40, wl.M),
+                                     np.arange(31, wl.M, 1024), np.arange(32, wl.M, 1024),
+                                     rng.choice(wl.M, 64, replace=False)]))
+    _check(hidden, w, b, wt, ids, rows, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
+    # properties on every row
+    assert np.all((ids >= 0) & (ids < wl.E))
+    srt = np.sort(ids, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])                        # distinct experts
+    groups = ids // (wl.E // wl.G)
+    assert max(len(set(r)) for r in groups.tolist()) <= wl.TG       # within TG groups
+    np.testing.assert_allclose(wt.astype(np.float64).sum(1), 1.0, atol=1e-5)
+    assert np.all(wt > 0)
+
+
+def test_fused_router_deterministic():
+    rng = np.random.default_rng(9)
+    hidden, w, b = _inputs(rng, 300, 448)
+    a = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    c = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_fused_router_rejects_outside_range():
+    x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((100, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="compiled range"):
+        mr.route_fused_router(x, wr, 8, 8, 4, True)      # H % 64 != 0
