@@ -62,6 +62,123 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"({dt:.1f} s, single-threaded C oracle in double precision)"}
 
 
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_calls(launch, n_sets, stream, steps=400, warmup=40):
+    """Mean per-call time (us) of back-to-back launches, and mean kernel time
+    (us) from an event pair around each launch; launch(i) runs set i % n_sets."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        launch(i % n_sets)
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record(stream)
+    for i in range(steps):
+        launch(i % n_sets)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) * 1e3 / steps
+    ev = _events(2 * min(steps, 200))
+    for i in range(len(ev) // 2):
+        ev[2 * i].record(stream)
+        launch(i % n_sets)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    kern = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(len(ev) // 2)]))
+    return per_call, kern * 1e3
+
+
+def measure_all(out_path=None):
+    """Every workload (each config, the biased-grouped M sweep, the fused router)."""
+    import numpy as np
+    import torch
+
+    import moe_expert_routing_amd as mr
+    from workloads import (BIASED_GROUPED_M_SWEEP, WORKLOADS, make_bias, make_logits,
+                           make_router_inputs)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    results = []
+
+    def routing_case(name, M=None):
+        wl = WORKLOADS[name]
+        x = dev_tensor(make_logits(wl, M))
+        M = x.shape[0]
+        b = make_bias(wl)
+        b = None if b is None else dev_tensor(b)
+        lb = 4 if wl.dtype == "f32" else 2
+        nbytes = algorithmic_bytes(M, wl.E, wl.K, lb, bias=b is not None)
+        n_sets = max(1, min(64, -(-512 * 2**20 // (M * (wl.E * lb + 8 * wl.K)))))
+        xs = [x] + [x.clone() for _ in range(n_sets - 1)]
+        outs = [(torch.empty(M, wl.K, device=dev), torch.empty(M, wl.K, dtype=torch.int32,
+                                                               device=dev)) for _ in range(n_sets)]
+
+        def launch(i):
+            w, ids = outs[i]
+            if wl.entry == "route_topk_softmax":
+                mr.route_topk_softmax(xs[i], wl.K, wl.renormalize, w, ids, stream=stream)
+            elif wl.entry == "route_grouped_topk":
+                mr.route_grouped_topk(xs[i], wl.K, wl.G, wl.TG, wl.renormalize, wl.scoring, w, ids,
+                                      stream=stream)
+            else:
+                mr.route_biased_grouped_topk(xs[i], b, wl.K, wl.G, wl.TG, wl.renormalize, w, ids,
+                                             stream=stream)
+        per_call, kern = time_calls(launch, n_sets, stream)
+        r = {"workload": name, "entry": wl.entry, "M": M, "E": wl.E, "K": wl.K, "G": wl.G,
+             "TG": wl.TG, "logits": wl.dtype, "rotating_sets": n_sets,
+             "us_per_call": per_call, "kernel_us": kern, "tokens_per_s": M / (per_call * 1e-6),
+             "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
+             "frac_hbm_kernel": nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        results.append(r)
+        eprint(json.dumps(r))
+
+    routing_case("softmax_e8_k2")
+    routing_case("sigmoid_bias_e256_k8")
+    routing_case("grouped_softmax_e160")
+    for M in BIASED_GROUPED_M_SWEEP:
+        routing_case("biased_grouped_e256", M)
+
+    wl = WORKLOADS["fused_router_h7168"]
+    hidden, w = make_router_inputs(wl)
+    hd, wd = dev_tensor(hidden), dev_tensor(w)
+    bd = dev_tensor(make_bias(wl))
+    M, H, E = wl.M, wl.hidden_dim, wl.E
+    n_sets = 5
+    hs = [hd] + [hd.clone() for _ in range(n_sets - 1)]
+    outs = [(torch.empty(M, wl.K, device=dev), torch.empty(M, wl.K, dtype=torch.int32,
+                                                           device=dev)) for _ in range(n_sets)]
+
+    def launch_fr(i):
+        mr.route_fused_router(hs[i], wd, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", bd,
+                              "top2sum", outs[i][0], outs[i][1], stream=stream)
+    per_call, kern = time_calls(launch_fr, n_sets, stream, steps=200, warmup=20)
+    nbytes = M * H * 2 + H * E * 2 + E * 4 + M * wl.K * 8
+    flops = 2.0 * M * H * E
+    r = {"workload": wl.name, "entry": wl.entry, "M": M, "H": H, "E": E, "K": wl.K,
+         "rotating_sets": n_sets, "us_per_call": per_call, "kernel_us": kern,
+         "tokens_per_s": M / (per_call * 1e-6), "alg_bytes": nbytes,
+         "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
+         "frac_hbm_kernel": nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+         "TFLOPs_kernel": flops / (kern * 1e-6) / 1e12,
+         "frac_mfma_bf16_kernel": flops / (kern * 1e-6) / 2.5e15}
+    results.append(r)
+    eprint(json.dumps(r))
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump(results, f, indent=1)
+    return results
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,6 +187,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time every workload (stderr, and --all-out FILE as JSON)")
+    ap.add_argument("--all-out", default=None)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -233,6 +353,8 @@ def main():
                 "graph_us_per_call": graph_us},
         "wall_s_timed": wall,
     }
+    if args.all_configs:
+        measure_all(args.all_out)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -92,8 +92,7 @@ struct RawLane<float, VPL> {
 
 template <typename T, int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/,
           int SPLIT, int TL, int KMAX>
-__global__ __launch_bounds__(kWavesPerBlock* kWave)
-__attribute__((amdgpu_waves_per_eu(GRP != 0 ? 5 : 1))) void route_fast_kernel(
+__global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     const T* __restrict__ logits, const float* __restrict__ bias, int64_t M, int TG, int K,
     int renorm, float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     constexpr int E = LPR * VPL;
