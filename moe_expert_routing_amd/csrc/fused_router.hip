@@ -8,7 +8,8 @@
 // computed with v_mfma_f32_32x32x16_bf16.  Wave w owns experts [64w, 64w+64)
 // (two 32x32 accumulator tiles).  The hidden dimension is walked in steps of
 // 64; each step stages a 32x64 tile of hidden states and a 64x256 tile of W
-// in LDS (double-buffered, loads for the next step in flight during the MFMAs).
+// in LDS (double-buffered); register rings keep the loads of the next six
+// hidden-state tiles and the next three W tiles in flight.
 // W is stored expert-contiguous ([H][E]) but an MFMA B operand wants 8
 // consecutive k per lane, so each thread transposes an 8x8 bf16 block in
 // registers (v_perm_b32) on its way to an [expert][k] LDS layout; rows are
@@ -79,18 +80,31 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const int w_kb = t % 8, w_nb = t / 8;
     const uint16_t* w_src = w + (int64_t)(w_kb * 8) * kFrE + w_nb * 8;
 
-    uint4 ra, rw[8];
-    auto load_step = [&](int k0) {
-        ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + k0) : make_uint4(0, 0, 0, 0);
+    // Register rings: the hidden-state tile of step t is loaded DA steps
+    // ahead (it comes from HBM), the W tile DW steps ahead (L2-resident).
+    constexpr int DA = 6, DW = 3, UNROLL = 6;
+    static_assert(UNROLL % DA == 0 && UNROLL % DW == 0, "ring slots must be compile-time");
+    uint4 ra[DA], rw[DW][8];
+    // Hidden states are read once: non-temporal loads keep them from evicting
+    // W, which every workgroup re-reads, from L2.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    // Rows past M read row 0 (always valid) and are zeroed when staged, so the
+    // load itself is unconditional.
+    auto load_a = [&](int slot_a, int k0) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a_src + k0));
+        ra[slot_a] = make_uint4(v[0], v[1], v[2], v[3]);
+    };
+    auto load_w = [&](int slot_w, int k0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            rw[i] = *reinterpret_cast<const uint4*>(w_src + (int64_t)(k0 + i) * kFrE);
+            rw[slot_w][i] = *reinterpret_cast<const uint4*>(w_src + (int64_t)(k0 + i) * kFrE);
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](int buf, int slot_a, int slot_w) {
         unsigned char* st = smem + buf * kFrStage;
-        *reinterpret_cast<uint4*>(st + a_row * kFrRowBytes + a_kc * 16) = ra;
+        *reinterpret_cast<uint4*>(st + a_row * kFrRowBytes + a_kc * 16) =
+            a_ok ? ra[slot_a] : make_uint4(0, 0, 0, 0);
         uint4 tw[8];
-        transpose8x8(rw, tw);
+        transpose8x8(rw[slot_w], tw);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             *reinterpret_cast<uint4*>(st + kFrBufA + (w_nb * 8 + j) * kFrRowBytes + w_kb * 16) =
@@ -102,15 +116,17 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     for (int q = 0; q < 16; ++q) { acc[0][q] = 0.f; acc[1][q] = 0.f; }
 
     const int steps = H / kFrBK;
-    load_step(0);
-    store_step(0);
-    __syncthreads();
     const int frag_m = lane % 32;          // A row / B column within a 32-tile
     const int frag_k = 8 * (lane / 32);    // first of the lane's 8 k values
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < steps) load_step((s + 1) * kFrBK);
-        const unsigned char* st = smem + buf * kFrStage;
+    // One step: refill the ring slots freed by step s (staged during step s-1)
+    // with the tiles DA / DW steps ahead, run the MFMAs on the staged tile, stage
+    // step s+1, barrier.  Loads past the last step re-read the last tile rather
+    // than branch: without branches the compiler tracks the outstanding loads
+    // exactly and waits only for the ones a step needs.
+    auto step = [&](const int s, const int u) {
+        load_a(u % DA, min(s + DA, steps - 1) * kFrBK);
+        load_w(u % DW, min(s + DW, steps - 1) * kFrBK);
+        const unsigned char* st = smem + (s & 1) * kFrStage;
 #pragma unroll
         for (int kk = 0; kk < kFrBK / 16; ++kk) {
             const int koff = (kk * 16 + frag_k) * 2;
@@ -123,9 +139,24 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
                 acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[nt], 0, 0, 0);
             }
         }
-        if (s + 1 < steps) store_step(buf ^ 1);
+        store_step((s + 1) & 1, (u + 1) % DA, (u + 1) % DW);  // step s+1 (or a spare copy)
         __syncthreads();
+    };
+    // prologue: steps 0..DA-1 of A and 0..DW-1 of W in flight; step 0 staged
+#pragma unroll
+    for (int q = 0; q < DA; ++q) load_a(q, min(q, steps - 1) * kFrBK);
+#pragma unroll
+    for (int q = 0; q < DW; ++q) load_w(q, min(q, steps - 1) * kFrBK);
+    store_step(0, 0, 0);
+    __syncthreads();
+    int s0 = 0;
+    for (; s0 + UNROLL <= steps; s0 += UNROLL) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) step(s0 + u, u);
     }
+#pragma unroll
+    for (int u = 0; u < UNROLL - 1; ++u)
+        if (s0 + u < steps) step(s0 + u, u);
 
     // ---- epilogue: logits to LDS, then route the 32 rows (8 lanes per row)
     float* L = reinterpret_cast<float*>(smem);     // [32][256] fp32 logits
