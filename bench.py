@@ -26,6 +26,48 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "biased_grouped_e256"
 
 
+# HBM bytes per launch of the headline kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by a plain copy of known size; valid only for the
+# kernel sources they were taken on.
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "route_fast_biased_grouped_e256_m65536_traffic.txt")
+KERNEL_SOURCES = ("route_fast.hip", "route_tile.cuh", "route_common.cuh")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "moe_expert_routing_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch (fetch + write) if the stored counters match these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split("=", 1) for l in f if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}),
+          flush=True)
+
+
 def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -190,12 +232,17 @@ def main():
     ap.add_argument("--all-configs", action="store_true",
                     help="also time every workload (stderr, and --all-out FILE as JSON)")
     ap.add_argument("--all-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for HBM byte counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: routing is per token and needs no collective; "
               f"--gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -241,7 +288,7 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = M / (ms_per_step * 1e-3)
 
-    # per-launch kernel duration: an event pair around each launch
+    # an event pair around each single launch (adds the event overhead)
     n_pair = min(args.steps, 400)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_pair)]
@@ -251,7 +298,10 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
-    achieved = bytes_per_call / (kern_ms * 1e-3) / 1e9
+    # The timed region holds nothing but back-to-back launches of the routing
+    # kernel on this stream, so its average launch duration is ms_per_step
+    # (event pairs around single launches add the event overhead to each).
+    achieved = bytes_per_call / (ms_per_step * 1e-3) / 1e9
 
     # warm (cache-resident) figure for context
     for i in range(50):
@@ -345,8 +395,10 @@ def main():
                    "logits": "bf16 N(0, var 2)", "bias": "fp32 N(0, var 0.02)",
                    "rotating_sets": sets, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic()},
         "hbm_GBps_whole_step": bytes_per_call / (ms_per_step * 1e-3) / 1e9,
+        "kernel_us_timed_region": ms_per_step * 1e3,
         "kernel_us_event_pairs": kern_ms * 1e3,
         "warm_cache_us_per_call": warm_ms * 1e3,
         "M64": {"kernel_us_event_pairs": m64_kernel_us, "loop_us_per_call": m64_loop_us,
