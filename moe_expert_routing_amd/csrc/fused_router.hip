@@ -7,13 +7,22 @@
 //   logits[32][256] = hidden[32][H] x W[H][256],  bf16 x bf16 -> fp32,
 // computed with v_mfma_f32_32x32x16_bf16.  Wave w owns experts [64w, 64w+64)
 // (two 32x32 accumulator tiles).  The hidden dimension is walked in steps of
-// 64; each step stages a 32x64 tile of hidden states and a 64x256 tile of W
-// in LDS (double-buffered); register rings keep the loads of the next six
-// hidden-state tiles and the next three W tiles in flight.
-// W is stored expert-contiguous ([H][E]) but an MFMA B operand wants 8
-// consecutive k per lane, so each thread transposes an 8x8 bf16 block in
-// registers (v_perm_b32) on its way to an [expert][k] LDS layout; rows are
-// padded to 144 bytes so that fragment reads are bank-conflict free.
+// 64 through two rings of LDS stages ahead of the MFMAs:
+//   - every tile goes from global memory straight into LDS; a fifth wave
+//     copies the hidden states, the MFMA waves copy W;
+//     (global_load_lds_dwordx4: each lane moves 16 bytes, a wave 1 KiB);
+//     the W tile of a step is one contiguous 32 KiB block of W; hidden
+//     states (read once, from HBM) run 11 steps ahead, W (re-read by every
+//     workgroup, from L2) 2 steps ahead;
+//   - W stays in its natural [k][expert] layout in LDS and the MFMA B
+//     operand (8 consecutive k of one expert per lane) is read with the
+//     transposing LDS read ds_read_b64_tr_b16: within each 16-lane group,
+//     lane j receives element j%4 of the 8-byte rows addressed by lanes
+//     j/4, j/4+4, j/4+8 and j/4+12 -- so lane i points at 4 experts of
+//     k row i/4 and every lane gets 4 consecutive k of its expert;
+//   - 16-byte chunks are XOR-swizzled inside LDS rows (by the source address
+//     each lane picks, since a wave's direct-to-LDS write is contiguous) so
+//     that both fragment reads are free of bank conflicts.
 // After the last step the fp32 logits go to LDS and the same routing core as
 // the standalone kernel (route_tile.cuh) routes the 32 rows, 8 lanes per row.
 // The logits never leave the compute unit.
@@ -26,143 +35,206 @@
 namespace moe_route {
 namespace {
 
-constexpr int kFrRows = 32;                      // tokens per workgroup
-constexpr int kFrE = 256;                        // experts
-constexpr int kFrBK = 64;                        // hidden units per step
-constexpr int kFrThreads = 256;                  // 4 waves
-constexpr int kFrRowBytes = kFrBK * 2 + 16;      // padded LDS row (A row or W column)
-constexpr int kFrBufA = kFrRows * kFrRowBytes;   // 4608 B
-constexpr int kFrBufB = kFrE * kFrRowBytes;      // 36864 B
-constexpr int kFrStage = kFrBufA + kFrBufB;      // 41472 B per stage
-constexpr int kFrLds = 2 * kFrStage;             // 82944 B
-static_assert(kFrLds >= 2 * kFrRows * kFrE * 4, "epilogue reuses the staging buffers");
+constexpr int kFrRows = 32;                   // tokens per workgroup
+constexpr int kFrE = 256;                     // experts
+constexpr int kFrBK = 64;                     // hidden units per step
+constexpr int kFrMathWaves = 4;               // MFMA waves; each also copies W
+constexpr int kFrThreads = 64 * (kFrMathWaves + 1);  // + one wave that copies hidden states
+constexpr int kFrAStages = 12;                // hidden-state ring (HBM)
+constexpr int kFrWStages = 3;                 // W ring (L2-resident)
+constexpr int kFrAAhead = kFrAStages - 1;     // steps each ring runs ahead
+constexpr int kFrWAhead = kFrWStages - 1;
+static_assert(kFrAAhead >= kFrWAhead, "hidden states run at least as far ahead as W");
+constexpr int kFrABytes = kFrRows * kFrBK * 2;  // 4 KiB: [32 rows][64 k] bf16, 128 B rows
+constexpr int kFrWBytes = kFrBK * kFrE * 2;     // 32 KiB: [64 k][256 experts] bf16, 512 B rows
+constexpr int kFrACopies = kFrABytes / 1024;                  // 4 wave loads per step
+constexpr int kFrWCopies = kFrWBytes / 1024 / kFrMathWaves;   // 8 per MFMA wave per step
+static_assert(2 * kFrRows * kFrE * 4 <= 2 * kFrWBytes, "epilogue reuses two W stages");
+static_assert(kFrAStages * kFrABytes + kFrWStages * kFrWBytes + kFrE * 4 <= 160 * 1024,
+              "LDS of one workgroup");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-// 8x8 bf16 transpose: in[i] holds row i (8 values in 4 dwords); out[j]
-// receives column j.  Output dword d of column j packs element j of rows 2d
-// (low half) and 2d+1 (high half).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t o[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint4& lo4 = in[2 * d];
-            const uint4& hi4 = in[2 * d + 1];
-            const uint32_t lo = (j / 2 == 0) ? lo4.x : (j / 2 == 1) ? lo4.y : (j / 2 == 2) ? lo4.z : lo4.w;
-            const uint32_t hi = (j / 2 == 0) ? hi4.x : (j / 2 == 1) ? hi4.y : (j / 2 == 2) ? hi4.z : hi4.w;
-            o[d] = __builtin_amdgcn_perm(hi, lo, (j % 2) ? 0x07060302u : 0x05040100u);
-        }
-        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+// Direct-to-LDS copies (global_load_lds_dwordx4): lane l copies 16 bytes from
+// its global address to LDS byte lds + 16 l (lds goes in M0).  They are inline asm
+// so that the compiler neither waits for them on its own (its conservative
+// waits drain the whole ring) nor counts them; the ring below waits for them
+// explicitly, and the loop holds no other vector-memory loads.  The
+// instruction writes no register, so nothing of the wave is overwritten
+// while a copy is in flight.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds)
+                 : "memory");
 }
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t offset, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(offset), "s"(base),
+                 "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
+}
+
+// Workgroup barrier without a memory fence.  A fence here would make every
+// wave wait for all of its copies still in flight (they write LDS); the ring
+// instead waits explicitly for exactly the copies a step consumes.
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Swizzles of the 16-byte chunk index inside an LDS row.
+// A rows (8 chunks): chunk c of row m lives at c ^ ((m >> 1) & 7).
+// W rows (32 chunks): chunk c of k row k lives at c ^ (4 * (k & 3)).
+__device__ __forceinline__ int a_swz(int m, int c) { return c ^ ((m >> 1) & 7); }
+__device__ __forceinline__ int w_swz(int k, int c) { return c ^ (4 * (k & 3)); }
 
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
     const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
-    __shared__ __align__(16) unsigned char smem[kFrLds];
+    __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
+    __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
     __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
-    const int wv = t / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
     const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
 
-    // Load assignment.  A: thread t copies 16 bytes of row t/8 at k-chunk t%8.
-    // W: thread t copies the 8x8 block (k rows 8*(t%8).., experts 8*(t/8)..).
-    const int a_row = t / 8, a_kc = t % 8;
-    const bool a_ok = m0 + a_row < M;
-    const uint16_t* a_src = hidden + (a_ok ? (m0 + a_row) * H : 0) + a_kc * 8;
-    const int w_kb = t % 8, w_nb = t / 8;
-    const uint16_t* w_src = w + (int64_t)(w_kb * 8) * kFrE + w_nb * 8;
-
-    // Register rings: the hidden-state tile of step t is loaded DA steps
-    // ahead (it comes from HBM), the W tile DW steps ahead (L2-resident).
-    constexpr int DA = 6, DW = 3, UNROLL = 6;
-    static_assert(UNROLL % DA == 0 && UNROLL % DW == 0, "ring slots must be compile-time");
-    uint4 ra[DA], rw[DW][8];
-    // Hidden states are read once: non-temporal loads keep them from evicting
-    // W, which every workgroup re-reads, from L2.
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // Rows past M read row 0 (always valid) and are zeroed when staged, so the
-    // load itself is unconditional.
-    auto load_a = [&](int slot_a, int k0) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a_src + k0));
-        ra[slot_a] = make_uint4(v[0], v[1], v[2], v[3]);
-    };
-    auto load_w = [&](int slot_w, int k0) {
+    // Direct-to-LDS copy assignment: every copy writes a 1 KiB block, lane l
+    // its chunk l, and reads the global chunk that the swizzle puts there.
+    //   hidden-state wave: A block j (rows 8j .. 8j+7), j = 0..3; rows past M
+    //     read row M-1 (never stored);
+    //   MFMA wave w: W blocks 8w .. 8w+7 (k rows 2b, 2b+1 of block b).
+    // Hidden states come from HBM and W from L2.  Waits count a wave's own
+    // loads in issue order, so a wave that copied both would wait on the slow
+    // hidden-state loads whenever it needs a W tile; giving them to a wave of
+    // their own lets each ring keep its own distance.
+    const bool copier = wv == kFrMathWaves;
+    const uint16_t* a_src[kFrACopies];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rw[slot_w][i] = *reinterpret_cast<const uint4*>(w_src + (int64_t)(k0 + i) * kFrE);
-    };
-    auto store_step = [&](int buf, int slot_a, int slot_w) {
-        unsigned char* st = smem + buf * kFrStage;
-        *reinterpret_cast<uint4*>(st + a_row * kFrRowBytes + a_kc * 16) =
-            a_ok ? ra[slot_a] : make_uint4(0, 0, 0, 0);
-        uint4 tw[8];
-        transpose8x8(rw[slot_w], tw);
+    for (int j = 0; j < kFrACopies; ++j) {
+        const int m = 8 * j + lane / 8;
+        a_src[j] = hidden + min(m0 + m, M - 1) * H + 8 * a_swz(m, lane % 8);
+    }
+    uint32_t w_off[kFrWCopies];  // byte offset inside a step's W block
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4*>(st + kFrBufA + (w_nb * 8 + j) * kFrRowBytes + w_kb * 16) =
-                tw[j];
+    for (int j = 0; j < kFrWCopies; ++j) {
+        const int k = 2 * (kFrWCopies * wv + j) + lane / 32;
+        w_off[j] = 2u * (k * kFrE + 8 * w_swz(k, lane % 32));
+    }
+    auto issue_a = [&](int step, int stage) {
+#pragma unroll
+        for (int j = 0; j < kFrACopies; ++j)
+            lds_copy16(a_src[j] + step * kFrBK, lds_addr(sA[stage] + 1024 * j));
+    };
+    // W copies j0 .. j0+n-1 of a step.
+    auto issue_w = [&](int step, int stage, int j0, int n) {
+        const uint16_t* wk = w + (int64_t)step * kFrBK * kFrE;
+#pragma unroll
+        for (int j = j0; j < j0 + n; ++j)
+            lds_copy16(wk, w_off[j], lds_addr(sW[stage] + 1024 * (kFrWCopies * wv + j)));
     };
 
+    // Fragment addresses.  A: lane l reads row l%32, k chunk 2kk + l/32.
+    // B (tile nt, k half h): lane l of 16-lane group g points at k row
+    // 16kk + 8(g/2) + 4h + (l%16)/4 and experts n0 + 16(g%2) + 4(l%4) .. +3.
+    const int fa_m = lane % 32;
+    const int g = lane / 16, gi = lane % 16;
     f32x16 acc[2];
 #pragma unroll
     for (int q = 0; q < 16; ++q) { acc[0][q] = 0.f; acc[1][q] = 0.f; }
 
-    const int steps = H / kFrBK;
-    const int frag_m = lane % 32;          // A row / B column within a 32-tile
-    const int frag_k = 8 * (lane / 32);    // first of the lane's 8 k values
-    // One step: refill the ring slots freed by step s (staged during step s-1)
-    // with the tiles DA / DW steps ahead, run the MFMAs on the staged tile, stage
-    // step s+1, barrier.  Loads past the last step re-read the last tile rather
-    // than branch: without branches the compiler tracks the outstanding loads
-    // exactly and waits only for the ones a step needs.
-    auto step = [&](const int s, const int u) {
-        load_a(u % DA, min(s + DA, steps - 1) * kFrBK);
-        load_w(u % DW, min(s + DW, steps - 1) * kFrBK);
-        const unsigned char* st = smem + (s & 1) * kFrStage;
+    // The MFMAs of one step.  All fragments of the step are read first (so
+    // the LDS latency is paid once, not per k slice); before the MFMAs of k
+    // slice kk it calls copies(kk), which issues a share of the next copies,
+    // so that issuing them (the address unit takes a 1 KiB wave load every
+    // 16 cycles) overlaps the math.
+    auto compute = [&](const unsigned char* a_base, const unsigned char* w_base, auto copies) {
+        bf16x8 af[kFrBK / 16], bfr[kFrBK / 16][2];
 #pragma unroll
         for (int kk = 0; kk < kFrBK / 16; ++kk) {
-            const int koff = (kk * 16 + frag_k) * 2;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + frag_m * kFrRowBytes + koff);
+            const int ac = 2 * kk + lane / 32;
+            af[kk] = *reinterpret_cast<const bf16x8*>(a_base + fa_m * 128 + 16 * a_swz(fa_m, ac));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const int n = wv * 64 + nt * 32 + frag_m;
-                const bf16x8 b =
-                    *reinterpret_cast<const bf16x8*>(st + kFrBufA + n * kFrRowBytes + koff);
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[nt], 0, 0, 0);
+                const int e = wv * 64 + nt * 32 + 16 * (g % 2) + 4 * (gi % 4);
+                i16x4 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 16 * kk + 8 * (g / 2) + 4 * h + gi / 4;
+                    const int off = k * 512 + 16 * w_swz(k, e / 8) + 2 * (e % 8);
+                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(w_base + off));
+                }
+                bfr[kk][nt] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
-        store_step((s + 1) & 1, (u + 1) % DA, (u + 1) % DW);  // step s+1 (or a spare copy)
-        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kFrBK / 16; ++kk) {
+            copies(kk);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk][nt], acc[nt], 0,
+                                                                  0, 0);
+        }
     };
-    // prologue: steps 0..DA-1 of A and 0..DW-1 of W in flight; step 0 staged
-#pragma unroll
-    for (int q = 0; q < DA; ++q) load_a(q, min(q, steps - 1) * kFrBK);
-#pragma unroll
-    for (int q = 0; q < DW; ++q) load_w(q, min(q, steps - 1) * kFrBK);
-    store_step(0, 0, 0);
-    __syncthreads();
-    int s0 = 0;
-    for (; s0 + UNROLL <= steps; s0 += UNROLL) {
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) step(s0 + u, u);
+
+    // Rings.  At step s the hidden-state wave issues the copies of step
+    // s + kFrAAhead and each MFMA wave those of W for step s + kFrWAhead (spread
+    // over its MFMAs); the prologues issue what the steps before step 0 would
+    // have.  At the top of step s a wave's loads issued after those of step s
+    // belong to the kFrAAhead - 1 (kFrWAhead - 1) later steps, so waiting until
+    // at most that many remain completes step s.  The barrier then makes every
+    // wave's copies visible and retires the reads of step s-1, whose stages the
+    // copies of step s reuse.  Copies past the last step repeat it into a stage
+    // that is never read again, so the count in flight is the same at every
+    // step.  Both kinds of wave pass the same number of barriers.
+    const int steps = H / kFrBK;
+    if (copier) {
+        for (int q = 0; q < kFrAAhead; ++q) issue_a(min(q, steps - 1), q);
+        int ia = 0;
+        for (int s = 0; s < steps; ++s) {
+            wait_vmcnt<kFrACopies * (kFrAAhead - 1)>();
+            barrier_no_fence();
+            issue_a(min(s + kFrAAhead, steps - 1), ia == 0 ? kFrAStages - 1 : ia - 1);
+            ia = ia == kFrAStages - 1 ? 0 : ia + 1;
+        }
+    } else {
+        for (int q = 0; q < kFrWAhead; ++q) issue_w(min(q, steps - 1), q, 0, kFrWCopies);
+        int ia = 0, iw = 0;  // stages of step s
+        for (int s = 0; s < steps; ++s) {
+            wait_vmcnt<kFrWCopies * (kFrWAhead - 1)>();
+            barrier_no_fence();
+            const int w_step = min(s + kFrWAhead, steps - 1);
+            const int w_stage = iw == 0 ? kFrWStages - 1 : iw - 1;
+            compute(sA[ia], sW[iw], [&](int kk) {
+                issue_w(w_step, w_stage, kk * kFrWCopies / 4, kFrWCopies / 4);
+            });
+            ia = ia == kFrAStages - 1 ? 0 : ia + 1;
+            iw = iw == kFrWStages - 1 ? 0 : iw + 1;
+        }
     }
-#pragma unroll
-    for (int u = 0; u < UNROLL - 1; ++u)
-        if (s0 + u < steps) step(s0 + u, u);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 
     // ---- epilogue: logits to LDS, then route the 32 rows (8 lanes per row)
-    float* L = reinterpret_cast<float*>(smem);     // [32][256] fp32 logits
-    float* S = L + kFrRows * kFrE;                 // [32][256] routing scratch
+    float* L = reinterpret_cast<float*>(sW[0]);  // [32][256] fp32 logits
+    float* S = reinterpret_cast<float*>(sW[1]);  // [32][256] routing scratch
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < 2 && !copier; ++nt) {
         const int n = wv * 64 + nt * 32 + (lane % 32);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -170,8 +242,9 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
             L[m * kFrE + n] = acc[nt][j];
         }
     }
-    if constexpr (BIAS) s_bias[t] = bias[t];
+    if (BIAS && t < kFrE) s_bias[t] = bias[t];
     __syncthreads();
+    if (copier) return;
 
     const int r = t / 8, sub = t % 8, rw_in_wave = (t % kWave) / 8;
     KeyParams kp;
