@@ -9,7 +9,8 @@
 //
 // Steps ("[SGLang] MoE routing: token-to-expert assignment algorithms"):
 //   1. scores: sigmoid, or softmax over the row (sections 2 and 4);
-//      selection score c = s + correction_bias (section 4).
+//      selection score c = s + correction_bias (section 4), kept in a
+//      per-wave LDS tile.
 //   2. group score per lane: max or top-2 sum of c (sections 3 and 4), then
 //      the rank of every group among the row's groups by a DPP all-to-all;
 //      the best topk_group groups survive (ties: lower group index).
@@ -17,17 +18,16 @@
 //      through LDS; each lane turns its candidates into 32-bit keys
 //          key = fixed_point(c) << 9 | (511 - expert)
 //      whose unsigned order is (c desc, expert asc), and keeps a sorted list
-//      of its T best keys (v_max / v_med3 insertion).
+//      of its K best keys (v_max / v_med3 insertion).
 //   4. K merge rounds: the row maximum of the list heads (DPP) is the next
 //      pick; its lane pops its head.
-//   5. weights: the unbiased score of each pick (recomputed from its logit),
-//      optionally renormalised; coalesced stores.
+//   5. weights: the unbiased score of each pick (c - bias, read back from
+//      LDS), optionally renormalised; stores.
 // The fixed-point step is 2^-23 * R, with R the smallest power of two above
 // the range of c (2 for softmax or unbiased sigmoid).  Keys therefore order
 // the selection scores exactly up to about 2.4e-7 for R = 2.  When the bias
-// spread would make that step coarser than 4.8e-7 (R > 4), or when a lane's
-// list runs dry while it still holds candidates, the wave redoes the
-// selection with exact (value, index) comparisons on the fp32 scores.
+// spread would make that step coarser than 4.8e-7 (R > 4), the wave redoes
+// the selection with exact (value, index) comparisons on the fp32 scores.
 #include <hip/hip_runtime.h>
 
 #include "route_common.cuh"
@@ -54,10 +54,6 @@ struct RawLane<uint16_t, VPL> {
 #pragma unroll
         for (int v = 0; v < VPL / 8; ++v) q[v] = reinterpret_cast<const uint4*>(p)[v];
     }
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int v = 0; v < VPL / 8; ++v) q[v] = make_uint4(0, 0, 0, 0);
-    }
     __device__ __forceinline__ void unpack(float (&x)[VPL]) const {
 #pragma unroll
         for (int v = 0; v < VPL / 8; ++v) {
@@ -77,10 +73,6 @@ struct RawLane<float, VPL> {
     __device__ __forceinline__ void load(const float* __restrict__ p) {
 #pragma unroll
         for (int v = 0; v < VPL / 4; ++v) q[v] = reinterpret_cast<const float4*>(p)[v];
-    }
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int v = 0; v < VPL / 4; ++v) q[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __device__ __forceinline__ void unpack(float (&x)[VPL]) const {
 #pragma unroll
@@ -118,47 +110,50 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     const int64_t tiles = (M + RPW - 1) / RPW;
     const int64_t tstride = (int64_t)gridDim.x * kWavesPerBlock;
     int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + wv;
-    RawLane<T, VPL> cur;  // first tile: its loads go out before the prologue below
-    cur.zero();
-    if (tile < tiles && tile * RPW + rw < M) cur.load(logits + (tile * RPW + rw) * E + sub * VPL);
+    // Rows of a tile past M read row M-1 (computed, never stored).
+    auto load_tile = [&](RawLane<T, VPL>& r, int64_t t) {
+        const int64_t row = min(t * RPW + rw, M - 1);
+        r.load(logits + row * E + sub * VPL);
+    };
+    RawLane<T, VPL> ra, rb;  // ping-pong: one tile routed while the next loads
+    if (tile < tiles) load_tile(ra, tile);  // in flight during the prologue below
 
-    // ---- key window.  Keys are compared only within a row, and each row's
-    // lanes together hold the whole bias, so a reduction over the row's lanes
-    // gives the range of the selection scores c = s + bias.
+    // ---- key window.  Keys are compared only within a row; the window holds
+    // every selection score c = s + bias of any row, so it comes from the
+    // range of the bias, reduced over the wave.
     KeyParams kp;
     if constexpr (BIAS) {
-        const float4* bq = reinterpret_cast<const float4*>(bias + sub * VPL);
         float bmin = INFINITY, bmax = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < CPL; ++v) {
-            const float4 d = bq[v];
+        for (int e = 4 * lane; e < E; e += 4 * kWave) {
+            const float4 d = *reinterpret_cast<const float4*>(bias + e);
             bmin = fminf(fminf(bmin, d.x), fminf(d.y, fminf(d.z, d.w)));
             bmax = fmaxf(fmaxf(bmax, d.x), fmaxf(d.y, fmaxf(d.z, d.w)));
         }
-        kp = key_params(row_min<LPR>(bmin), 1.0f + row_max<LPR>(bmax));
+        kp = key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
         for (int e = threadIdx.x; e < E; e += kWavesPerBlock * kWave) s_bias[e] = bias[e];
         __syncthreads();
     } else {
         kp = key_params(0.0f, 1.0f);
     }
 
-    for (; tile < tiles; tile += tstride) {
-        const int64_t row = tile * RPW + rw;
+    auto route_tile = [&](const RawLane<T, VPL>& r, int64_t t) {
+        const int64_t row = t * RPW + rw;
         const bool valid = row < M;
-        RawLane<T, VPL> nxt;  // prefetch the next tile of this wave
-        nxt.zero();
-        {
-            const int64_t nrow = (tile + tstride) * RPW + rw;
-            if (tile + tstride < tiles && nrow < M) nxt.load(logits + nrow * E + sub * VPL);
-        }
-
         float x[VPL];
-        cur.unpack(x);
+        r.unpack(x);
         const T* xr = logits + (valid ? row : 0) * E;
         route_rows<LPR, VPL, SOFTMAX, BIAS, GRP, SPLIT, TL, KMAX>(
             x, sub, rw, valid, row, my_row, s_bias, kp, TG, K, renorm, w_out, id_out,
             [&](int e) { return load_one<T>(xr, e); });
-        cur = nxt;
+    };
+    while (tile < tiles) {
+        if (tile + tstride < tiles) load_tile(rb, tile + tstride);
+        route_tile(ra, tile);
+        tile += tstride;
+        if (tile >= tiles) break;
+        if (tile + tstride < tiles) load_tile(ra, tile + tstride);
+        route_tile(rb, tile);
+        tile += tstride;
     }
 }
 

@@ -187,7 +187,7 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
     // max rule, (h - 2 lo) * scale for the top-2 sum; both lie in [0, 2^24).
     const float h_offs = (GRP == 2 ? 2.0f : 1.0f) * (kp.offs - 8388608.0f);
 
-    // ---- 1. scores s (stored to LDS) and selection scores c = s + bias
+    // ---- 1. scores s and selection scores c = s + bias (c stored to LDS)
     float mx = 0.f, row_total = 1.f;
     if constexpr (SOFTMAX) {
         float m = x[0];
@@ -204,18 +204,18 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         }
         if constexpr (SOFTMAX) row_total = row_sum<LPR>(acc);
     }
-    if constexpr (LPR > 1) {
-#pragma unroll
-        for (int v = 0; v < CPL; ++v)
-            reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v)] =
-                make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
-    }
     if constexpr (BIAS) {
 #pragma unroll
         for (int v = 0; v < CPL; ++v) {
             const float4 d = reinterpret_cast<const float4*>(s_bias + sub * VPL)[v];
             x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
         }
+    }
+    if constexpr (LPR > 1) {
+#pragma unroll
+        for (int v = 0; v < CPL; ++v)
+            reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v)] =
+                make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
     }
     // x now holds the selection scores c of the lane's experts
 
@@ -265,20 +265,9 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
                     my_row)[tile_chunk<ROW>((cand_base >> 2) + v)];
                 cc[4 * v] = d.x; cc[4 * v + 1] = d.y; cc[4 * v + 2] = d.z; cc[4 * v + 3] = d.w;
             }
-            if constexpr (BIAS) {
-#pragma unroll
-                for (int v = 0; v < NC / 4; ++v) {
-                    const float4 d = reinterpret_cast<const float4*>(s_bias + cand_base)[v];
-                    cc[4 * v] += d.x; cc[4 * v + 1] += d.y;
-                    cc[4 * v + 2] += d.z; cc[4 * v + 3] += d.w;
-                }
-            }
         } else {
 #pragma unroll
-            for (int j = 0; j < NC; ++j) {
-                cc[j] = my_row[tile_elem<ROW>(cand_base + j)];
-                if constexpr (BIAS) cc[j] += s_bias[cand_base + j];
-            }
+            for (int j = 0; j < NC; ++j) cc[j] = my_row[tile_elem<ROW>(cand_base + j)];
         }
     } else {
 #pragma unroll
@@ -383,7 +372,10 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         pick[s] = min(max(pick[s], 0), E - 1);  // never read outside the row
         float sv;
         if constexpr (LPR > 1) {
+            // the row holds c; the weight is the unbiased score c - bias
+            // (within a few fp32 ulps of s)
             sv = my_row[tile_elem<ROW>(pick[s])];
+            if constexpr (BIAS) sv -= s_bias[pick[s]];
         } else if constexpr (SOFTMAX) {
             sv = x[0];  // one lane per row: x holds the numerators
 #pragma unroll
