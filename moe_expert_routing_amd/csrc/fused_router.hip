@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     }
     const int64_t row = m0 + r;
     const float* lrow = L + r * kFrE;
-    route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), 8, 8>(
+    route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
         x, sub, rw_in_wave, row < M, row, S + r * kFrE, s_bias, kp, TG, K, renorm, w_out,
         id_out, [&](int e) { return lrow[e]; });
 }

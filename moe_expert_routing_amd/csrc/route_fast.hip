@@ -18,7 +18,7 @@
 //      through LDS; each lane turns its candidates into 32-bit keys
 //          key = fixed_point(c) << 9 | (511 - expert)
 //      whose unsigned order is (c desc, expert asc), and keeps a sorted list
-//      of its K best keys (v_max / v_med3 insertion).
+//      of its 4 or 5 best keys (v_max / v_med3 insertion).
 //   4. K merge rounds: the row maximum of the list heads (DPP) is the next
 //      pick; its lane pops its head.
 //   5. weights: the unbiased score of each pick (c - bias, read back from
@@ -26,8 +26,9 @@
 // The fixed-point step is 2^-23 * R, with R the smallest power of two above
 // the range of c (2 for softmax or unbiased sigmoid).  Keys therefore order
 // the selection scores exactly up to about 2.4e-7 for R = 2.  When the bias
-// spread would make that step coarser than 4.8e-7 (R > 4), the wave redoes
-// the selection with exact (value, index) comparisons on the fp32 scores.
+// spread would make that step coarser than 4.8e-7 (R > 4), or when a lane
+// dropped a key that beats the K-th pick, the wave redoes the selection with
+// exact (value, index) comparisons on the fp32 scores.
 #include <hip/hip_runtime.h>
 
 #include "route_common.cuh"
@@ -198,27 +199,31 @@ route_status_t launch_fast(const RouteProblem& p) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // E = 256 (or 160) with one group per lane (G == 8) or no groups.  With
-// groups, each surviving group is split over two lanes; a lane's list is as
-// long as K (<= 8), so it can always supply every pick that falls to it.
+// groups, each surviving group is split over two lanes.  A lane keeps its 4
+// (grouped) or 5 (ungrouped, more candidates per lane) best keys; on the
+// synthetic workloads a row needs more than that from one lane in well under
+// 1% of waves, which then take the exact path.
 template <typename T, int VPL, int KMAX>
 route_status_t dispatch_lpr8_k(const RouteProblem& p, bool& handled) {
+    constexpr int TLU = KMAX < 5 ? KMAX : 5;  // list length, ungrouped
+    constexpr int TLG = KMAX < 4 ? KMAX : 4;  // list length, grouped
     handled = true;
     const bool soft = p.scoring == ROUTE_SOFTMAX;
     const bool bias = p.bias != nullptr;
     if (p.G == 1) {
-        if (soft) return launch_fast<T, 8, VPL, true, false, 0, 1, KMAX, KMAX>(p);
-        if (bias) return launch_fast<T, 8, VPL, false, true, 0, 1, KMAX, KMAX>(p);
-        return launch_fast<T, 8, VPL, false, false, 0, 1, KMAX, KMAX>(p);
+        if (soft) return launch_fast<T, 8, VPL, true, false, 0, 1, TLU, KMAX>(p);
+        if (bias) return launch_fast<T, 8, VPL, false, true, 0, 1, TLU, KMAX>(p);
+        return launch_fast<T, 8, VPL, false, false, 0, 1, TLU, KMAX>(p);
     }
     if (p.G == 8 && p.TG <= 4) {
         if (p.rule == ROUTE_GROUP_TOP2_SUM) {
             if (soft) { handled = false; return ROUTE_OK; }
-            if (bias) return launch_fast<T, 8, VPL, false, true, 2, 2, KMAX, KMAX>(p);
-            return launch_fast<T, 8, VPL, false, false, 2, 2, KMAX, KMAX>(p);
+            if (bias) return launch_fast<T, 8, VPL, false, true, 2, 2, TLG, KMAX>(p);
+            return launch_fast<T, 8, VPL, false, false, 2, 2, TLG, KMAX>(p);
         }
-        if (soft) return launch_fast<T, 8, VPL, true, false, 1, 2, KMAX, KMAX>(p);
-        if (bias) return launch_fast<T, 8, VPL, false, true, 1, 2, KMAX, KMAX>(p);
-        return launch_fast<T, 8, VPL, false, false, 1, 2, KMAX, KMAX>(p);
+        if (soft) return launch_fast<T, 8, VPL, true, false, 1, 2, TLG, KMAX>(p);
+        if (bias) return launch_fast<T, 8, VPL, false, true, 1, 2, TLG, KMAX>(p);
+        return launch_fast<T, 8, VPL, false, false, 1, 2, TLG, KMAX>(p);
     }
     handled = false;
     return ROUTE_OK;

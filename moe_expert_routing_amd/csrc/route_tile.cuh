@@ -96,13 +96,22 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
 }
 
 // Insert key k into the descending list L[0..T-1] (keys are unique): the new
-// t-th largest of {L, k} is the median of (L[t-1], L[t], k).
-template <int T>
-__device__ __forceinline__ void list_insert(uint32_t (&L)[T], uint32_t k) {
+// t-th largest of {L, k} is the median of (L[t-1], L[t], k).  The key that
+// drops out is min(L[T-1], k); ev keeps the largest key dropped so far.
+// Every dropped key is below every key still held, so ev <= L[T-1] and
+// max(ev, min(L[T-1], k)) is the median of (ev, L[T-1], k).
+template <int T, bool TRACK>
+__device__ __forceinline__ void list_insert(uint32_t (&L)[T], uint32_t k, uint32_t& ev) {
+    if constexpr (TRACK) ev = umed3(ev, L[T - 1], k);
 #pragma unroll
     for (int t = T - 1; t >= 1; --t) L[t] = umed3(L[t - 1], L[t], k);
     L[0] = max(L[0], k);
 }
+
+template <int N>
+struct ListLen {
+    static constexpr int value = N;
+};
 
 // Fixed-point key of a selection score: t = (c - lo) * 2^23 / R + 2^23 lies in
 // [2^23, 2^24), so its fp32 mantissa is the fixed-point value; shifting the
@@ -181,7 +190,11 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
     static_assert(E <= 512, "9 index bits");
     static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
     static_assert(GRP == 0 || LPR == 8, "grouped kernels hold one of 8 groups per lane");
-    static_assert(TL >= KMAX || TL >= NC, "a lane's list never runs dry");
+    static_assert(LPR > 1 || TL >= KMAX, "one lane per row reads its picks off its list");
+    // A lane keeps only its TL best keys.  When that can be fewer than a
+    // row needs from one lane, the keys it dropped are tracked, and a wave in
+    // which a dropped key beats the K-th pick selects again with longer lists.
+    constexpr bool TRACK = TL < KMAX && TL < NC;
     static_assert(VPL % 4 == 0 && SLOTS <= 2, "");
     // Group scores as fixed point with the key step: (h - lo) * scale for the
     // max rule, (h - 2 lo) * scale for the top-2 sum; both lie in [0, 2^24).
@@ -273,62 +286,96 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
 #pragma unroll
         for (int j = 0; j < NC; ++j) cc[j] = x[j];
     }
-    uint32_t L[TL];
-#pragma unroll
-    for (int t = 0; t < TL; ++t) L[t] = 0u;
-    if (has_cand) {
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-            list_insert<TL>(L, make_key(cc[j], kp.scale, kp.offs, (uint32_t)(NC - 1 - j)));
-    }
     // low 9 bits := 511 - expert index; empty slots stay below 512
     const uint32_t base9 = 511u - (uint32_t)(cand_base + NC - 1);
-#pragma unroll
-    for (int t = 0; t < TL; ++t) L[t] += base9;
 
-    // ---- 4. merge: K rounds of a row-wide maximum over the list heads
+    // ---- 4. per-lane lists of the T best keys, then K merge rounds: the
+    // row-wide maximum of the list heads is the next pick and its lane pops
+    // its head.  wk receives this lane's picks, w_last the K-th pick, ev the
+    // largest key a list dropped (when T can be short of what a row needs).
     uint32_t wk[SLOTS];
+    uint32_t w_last = 0u;
+    auto select = [&](auto t_c, uint32_t& ev) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr bool TR = T < KMAX && T < NC;
+        uint32_t L[T];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) wk[s] = 0u;
-    if constexpr (LPR == 1) {
+        for (int t = 0; t < T; ++t) L[t] = 0u;
+        if (has_cand) {
 #pragma unroll
-        for (int s = 0; s < SLOTS; ++s) wk[s] = L[s];
-    } else {
+            for (int j = 0; j < NC; ++j)
+                list_insert<T, TR>(L, make_key(cc[j], kp.scale, kp.offs, (uint32_t)(NC - 1 - j)),
+                                   ev);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) L[t] += base9;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) wk[s] = 0u;
+        if constexpr (LPR == 1) {
+#pragma unroll
+            for (int s = 0; s < SLOTS; ++s) wk[s] = L[s];
+        } else {
 #pragma unroll 1
-        for (int r = 0; r < K; ++r) {
-            const uint32_t w = row_max_u32<LPR>(L[0]);
-            const bool mine = (L[0] == w);
+            for (int r = 0; r < K; ++r) {
+                const uint32_t w = row_max_u32<LPR>(L[0]);
+                w_last = w;
+                const bool mine = (L[0] == w);
 #pragma unroll
-            for (int t = 0; t < TL - 1; ++t) L[t] = mine ? L[t + 1] : L[t];
-            L[TL - 1] = mine ? base9 : L[TL - 1];
-            if (sub == r % LPR) {
-                if (SLOTS == 1 || r < LPR) wk[0] = w;
-                else wk[SLOTS - 1] = w;
+                for (int t = 0; t < T - 1; ++t) L[t] = mine ? L[t + 1] : L[t];
+                L[T - 1] = mine ? base9 : L[T - 1];
+                if (sub == r % LPR) {
+                    if (SLOTS == 1 || r < LPR) wk[0] = w;
+                    else wk[SLOTS - 1] = w;
+                }
             }
+        }
+    };
+    uint32_t ev = 0u;
+    select(ListLen<TL>{}, ev);
+    if constexpr (TRACK) {
+        // A dropped key beats the K-th pick somewhere in the wave: redo the
+        // wave's selection with lists as long as K, which cannot run dry.
+        if (__ballot(ev != 0u && ev + base9 > w_last) != 0) {
+            uint32_t unused = 0u;
+            select(ListLen<KMAX>{}, unused);
         }
     }
     int pick[SLOTS];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) pick[s] = 511 - (int)(wk[s] & 511u);
 
-    // ---- exact path for a bias spread too wide for the key window: K
-    // rounds of a (value, index) argmax on the fp32 selection scores.
-    // Rolled loops and LDS re-reads keep this rare path off the register
-    // budget of the main path.
+    // ---- exact path, for a bias spread too wide for the key window: K
+    // rounds of a (value, index) argmax on the fp32 selection scores.  With
+    // several lanes per row the scores are read from the row's LDS tile, 16
+    // bytes at a time, in rolled loops that keep this rare path off the
+    // register budget of the main path.
     if (kp.exact_only) {
-        auto cval = [&](int e) {  // selection score c of expert e of this row
-            float v = lane_score<SOFTMAX>(logit_of(e), mx);
-            if constexpr (BIAS) v += s_bias[e];
-            return v;
+        // c of this lane's experts sub*VPL + 4q .. +3
+        auto chunk = [&](int q) -> float4 {
+            if constexpr (LPR > 1) {
+                return reinterpret_cast<const float4*>(my_row)[tile_chunk<ROW>(sub * CPL + q)];
+            } else {
+                float c4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    c4[i] = lane_score<SOFTMAX>(logit_of(4 * q + i), mx);
+                    if constexpr (BIAS) c4[i] += s_bias[4 * q + i];
+                }
+                return make_float4(c4[0], c4[1], c4[2], c4[3]);
+            }
         };
         bool kept = true;
         if constexpr (GRP != 0) {
             float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll 1
-            for (int j = 0; j < VPL; ++j) {
-                const float c = cval(sub * VPL + j);
-                if (GRP == 2) m2 = __builtin_amdgcn_fmed3f(m1, m2, c);
-                m1 = fmaxf(m1, c);
+            for (int q = 0; q < CPL; ++q) {
+                const float4 d = chunk(q);
+                const float c4[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (GRP == 2) m2 = __builtin_amdgcn_fmed3f(m1, m2, c4[i]);
+                    m1 = fmaxf(m1, c4[i]);
+                }
             }
             const float h = GRP == 2 ? m1 + m2 : m1;
             int rank = 0;
@@ -347,10 +394,17 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
             int bi = 0x7fffffff;
             if (kept) {
 #pragma unroll 1
-                for (int j = 0; j < VPL; ++j) {
-                    const int e = sub * VPL + j;
-                    const float v = cval(e);
-                    if (beats(bv_prev, bi_prev, v, e) && beats(v, e, bv, bi)) { bv = v; bi = e; }
+                for (int q = 0; q < CPL; ++q) {
+                    const float4 d = chunk(q);
+                    const float c4[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = sub * VPL + 4 * q + i;
+                        if (beats(bv_prev, bi_prev, c4[i], e) && beats(c4[i], e, bv, bi)) {
+                            bv = c4[i];
+                            bi = e;
+                        }
+                    }
                 }
             }
             row_argmax<LPR>(bv, bi);

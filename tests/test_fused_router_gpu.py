@@ -57,6 +57,21 @@ def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm):
     _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, renorm, scoring, rule)
 
 
+@pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
+def test_fused_router_one_lane_holds_most_picks(G, TG):
+    """A bias that lifts the first 16 experts puts most of the top 8 of a
+    row in one lane's candidates, more than its short list keeps: the
+    epilogue must take its exact path there."""
+    rng = np.random.default_rng(5 + G)
+    M, H = 160, 256
+    hidden, w, b = _inputs(rng, M, H)
+    b[:16] += np.float32(0.6)
+    log(f"[gpu] route_fused_router skewed bias G={G} TG={TG}")
+    wt, ids = _run(hidden, w, b, 8, G, TG, True, "sigmoid", "top2sum")
+    assert (ids < 16).sum(axis=1).mean() > 6  # most rows take 5+ picks from one lane
+    _check(hidden, w, b, wt, ids, np.arange(M), 8, G, TG, True, "sigmoid", "top2sum")
+
+
 def test_fused_router_full_workload_sampled():
     wl = WORKLOADS["fused_router_h7168"]
     hidden, w = make_router_inputs(wl)

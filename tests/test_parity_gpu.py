@@ -97,6 +97,39 @@ def test_exact_ties_resolve_by_index(entry, scoring):
     assert rep.ok() and rep.exact == M, rep.summary()
 
 
+@pytest.mark.parametrize("entry,E,G,TG,K,scoring,dtype,hot", [
+    ("route_biased_grouped_topk", 256, 8, 4, 8, "sigmoid", "bf16", 16),
+    ("route_grouped_topk", 256, 8, 4, 8, "sigmoid", "f32", 16),
+    ("route_biased_grouped_topk", 256, 1, 1, 8, "sigmoid", "bf16", 32),
+    ("route_topk_softmax", 256, 1, 1, 8, "softmax", "f32", 32),
+    ("route_grouped_topk", 160, 8, 3, 6, "softmax", "f32", 10),
+])
+def test_one_lane_holds_most_picks(entry, E, G, TG, K, scoring, dtype, hot):
+    """About half the rows have their whole top K among the first `hot`
+    experts, the candidates one lane of the kernel holds: more picks than
+    its short list keeps, so those waves must take the exact path.  The
+    other rows are ordinary, so waves mix both kinds."""
+    rng = np.random.default_rng(E * 10 + K)
+    M = 1000
+    xf = rng.standard_normal((M, E), dtype=np.float32)
+    hot_rows = rng.random(M) < 0.5
+    xf[hot_rows, :hot] += np.float32(6.0)
+    x = bf16_bits_from_f32(xf) if dtype == "bf16" else xf
+    b = None
+    if entry == "route_biased_grouped_topk":
+        # small, so that the bias does not undo the lift of the hot experts
+        b = rng.standard_normal(E, dtype=np.float32) * np.float32(0.01)
+    log(f"[gpu] one lane holds most picks: {entry} E={E} G={G} TG={TG} K={K} hot={hot}")
+    w, ids = route_gpu(entry, to_device(x), K=K, G=G, TG=TG, scoring=scoring,
+                       bias=None if b is None else to_device(b), renorm=True)
+    # the premise: most hot rows take all K picks from the hot experts
+    assert (ids[hot_rows] < hot).all(axis=1).mean() > 0.9
+    sc, rule = oracle_args(entry, scoring)
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=G, TG=TG, rule=rule, K=K, renorm=True)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+
+
 def test_empty_batch():
     wl = WORKLOADS["biased_grouped_e256"]
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
