@@ -242,14 +242,14 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
             L[m * kFrE + n] = acc[nt][j];
         }
     }
-    if (BIAS && t < kFrE) s_bias[t] = bias[t];
+    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
     __syncthreads();
     if (copier) return;
 
     const int r = t / 8, sub = t % 8, rw_in_wave = (t % kWave) / 8;
     KeyParams kp;
     if constexpr (BIAS) {
-        float bmin = INFINITY, bmax = -INFINITY;
+        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
             bmin = fminf(bmin, s_bias[sub * 32 + j]);

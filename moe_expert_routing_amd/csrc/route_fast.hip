@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
             bmax = fmaxf(fmaxf(bmax, d.x), fmaxf(d.y, fmaxf(d.z, d.w)));
         }
         kp = key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
-        for (int e = threadIdx.x; e < E; e += kWavesPerBlock * kWave) s_bias[e] = bias[e];
+        for (int e = threadIdx.x; e < E; e += kWavesPerBlock * kWave) s_bias[bias_elem<E>(e)] = bias[e];
         __syncthreads();
     } else {
         kp = key_params(0.0f, 1.0f);

@@ -149,16 +149,27 @@ __device__ __forceinline__ KeyParams key_params(float cmin, float cmax) {
 
 // Offsets inside a row of the per-wave LDS tile (ROW fp32 values); 16-byte
 // chunks are permuted within aligned blocks of 8 (see swz_chunk) when the row
-// spans whole blocks.
+// spans whole blocks, and rows of odd index (rw, the row within the wave)
+// also swap neighbouring blocks when the row spans whole pairs of blocks.
+// With 8 lanes per row writing the same chunk number of 8 rows, the 64 lanes
+// of a store then cover all 16 bank groups, 4 lanes each.
 template <int ROW>
-__device__ __forceinline__ int tile_chunk(int q) {
-    if constexpr ((ROW / 4) % 8 == 0) return swz_chunk(q);
+__device__ __forceinline__ int tile_chunk(int q, int rw) {
+    if constexpr ((ROW / 4) % 16 == 0) return swz_chunk(q) ^ (8 * (rw & 1));
+    else if constexpr ((ROW / 4) % 8 == 0) return swz_chunk(q);
     return q;
 }
 template <int ROW>
-__device__ __forceinline__ int tile_elem(int i) {
-    return tile_chunk<ROW>(i >> 2) * 4 + (i & 3);
+__device__ __forceinline__ int tile_elem(int i, int rw) {
+    return tile_chunk<ROW>(i >> 2, rw) * 4 + (i & 3);
 }
+// Layout of the bias staged in LDS (E values): chunks permuted like a tile
+// row, so that the 8 lanes of a row, reading the same chunk number of their
+// own 32 (or 20) experts, hit different bank groups.
+template <int E>
+__device__ __forceinline__ int bias_chunk(int q) { return tile_chunk<E>(q, 0); }
+template <int E>
+__device__ __forceinline__ int bias_elem(int e) { return tile_elem<E>(e, 0); }
 
 // Unbiased score of a logit: sigmoid, or the softmax numerator exp(x - max).
 template <bool SOFTMAX>
@@ -170,7 +181,8 @@ __device__ __forceinline__ float lane_score(float x, float mx) {
 // Route the rows of one wave tile.  Lane `sub` of row-in-wave `rw` brings the
 // fp32 logits x[0..VPL) of experts [sub*VPL, sub*VPL + VPL) of token `row`
 // (valid == false past the last token: computed, never stored).  my_row is
-// this row's E-float LDS scratch (LPR > 1); s_bias the bias in LDS (BIAS);
+// this row's E-float LDS scratch (LPR > 1); s_bias the bias in LDS, in the
+// bias_elem layout (BIAS);
 // logit_of(e) returns the fp32 logit of expert e of this row (rare paths).
 // Steps follow "[SGLang] MoE routing: token-to-expert assignment algorithms",
 // sections 2-4; see the file header of route_fast.hip for the design.
@@ -220,14 +232,14 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
     if constexpr (BIAS) {
 #pragma unroll
         for (int v = 0; v < CPL; ++v) {
-            const float4 d = reinterpret_cast<const float4*>(s_bias + sub * VPL)[v];
+            const float4 d = reinterpret_cast<const float4*>(s_bias)[bias_chunk<E>(sub * CPL + v)];
             x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
         }
     }
     if constexpr (LPR > 1) {
 #pragma unroll
         for (int v = 0; v < CPL; ++v)
-            reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v)] =
+            reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v, rw)] =
                 make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
     }
     // x now holds the selection scores c of the lane's experts
@@ -275,12 +287,12 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
 #pragma unroll
             for (int v = 0; v < NC / 4; ++v) {
                 const float4 d = reinterpret_cast<const float4*>(
-                    my_row)[tile_chunk<ROW>((cand_base >> 2) + v)];
+                    my_row)[tile_chunk<ROW>((cand_base >> 2) + v, rw)];
                 cc[4 * v] = d.x; cc[4 * v + 1] = d.y; cc[4 * v + 2] = d.z; cc[4 * v + 3] = d.w;
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < NC; ++j) cc[j] = my_row[tile_elem<ROW>(cand_base + j)];
+            for (int j = 0; j < NC; ++j) cc[j] = my_row[tile_elem<ROW>(cand_base + j, rw)];
         }
     } else {
 #pragma unroll
@@ -353,13 +365,13 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         // c of this lane's experts sub*VPL + 4q .. +3
         auto chunk = [&](int q) -> float4 {
             if constexpr (LPR > 1) {
-                return reinterpret_cast<const float4*>(my_row)[tile_chunk<ROW>(sub * CPL + q)];
+                return reinterpret_cast<const float4*>(my_row)[tile_chunk<ROW>(sub * CPL + q, rw)];
             } else {
                 float c4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     c4[i] = lane_score<SOFTMAX>(logit_of(4 * q + i), mx);
-                    if constexpr (BIAS) c4[i] += s_bias[4 * q + i];
+                    if constexpr (BIAS) c4[i] += s_bias[bias_elem<E>(4 * q + i)];
                 }
                 return make_float4(c4[0], c4[1], c4[2], c4[3]);
             }
@@ -428,8 +440,8 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         if constexpr (LPR > 1) {
             // the row holds c; the weight is the unbiased score c - bias
             // (within a few fp32 ulps of s)
-            sv = my_row[tile_elem<ROW>(pick[s])];
-            if constexpr (BIAS) sv -= s_bias[pick[s]];
+            sv = my_row[tile_elem<ROW>(pick[s], rw)];
+            if constexpr (BIAS) sv -= s_bias[bias_elem<E>(pick[s])];
         } else if constexpr (SOFTMAX) {
             sv = x[0];  // one lane per row: x holds the numerators
 #pragma unroll
