@@ -54,6 +54,8 @@ def _load():
         lib.oracle_group_scores.restype = i32
         lib.oracle_router_logits.argtypes = [p, p, i64, i32, i32, p]
         lib.oracle_router_logits.restype = i32
+        lib.oracle_dispatch.argtypes = [p, p, i64, i32, p, p, p, p, p]
+        lib.oracle_dispatch.restype = i32
         _lib = lib
     return _lib
 
@@ -134,3 +136,24 @@ def router_logits(hidden_bits, w_bits):
     if lib.oracle_router_logits(_ptr(a), _ptr(b), M, H, E, _ptr(out)):
         raise ValueError("oracle_router_logits: bad arguments")
     return out
+
+
+def dispatch(topk_ids, num_experts, topk_weights=None):
+    """Expert-sorted dispatch metadata of a routing result (stable counting
+    sort of the flattened assignments by expert id; ids outside
+    [0, num_experts) are dropped).  Returns (counts [E], offsets [E+1],
+    gather [n], scatter [n], sorted_weights [n] or None), n = topk_ids.size."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(-1)
+    n = ids.size
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights,
+                                                               dtype=np.float32).reshape(-1)
+    counts = np.empty(num_experts, np.int32)
+    offsets = np.empty(num_experts + 1, np.int32)
+    gather = np.empty(n, np.int32)
+    scatter = np.empty(n, np.int32)
+    sw = None if w is None else np.empty(n, np.float32)
+    rc = _load().oracle_dispatch(_ptr(ids), _ptr(w), n, num_experts, _ptr(counts),
+                                 _ptr(offsets), _ptr(gather), _ptr(scatter), _ptr(sw))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch rejected its arguments (code {rc})")
+    return counts, offsets, gather, scatter, sw

@@ -264,3 +264,52 @@ int oracle_router_logits(const uint16_t* hidden, const uint16_t* w, int64_t M, i
     }
     return 0;
 }
+
+/*
+ * Expert-sorted dispatch metadata of a routing result.  The routing page
+ * ([ROUTING], section "output format") names a kernel-oriented output made of
+ * routing data, a gather index and a scatter index, without defining their
+ * fields.  The reading taken here is the plainest one: the M*K (token, slot)
+ * assignments, numbered a = m*K + k, are put in order of expert id, and
+ * assignments of the same expert keep their order a (a stable counting sort):
+ *   counts[e]   number of assignments to expert e;
+ *   offsets[e]  where expert e's run starts (exclusive prefix sum of counts;
+ *               offsets[E] = number of valid assignments);
+ *   gather[p]   the assignment at sorted position p (-1 past offsets[E]);
+ *   scatter[a]  the sorted position of assignment a (its inverse), or -1 when
+ *               ids[a] is outside [0, E) (such an assignment is dropped);
+ *   sorted_w[p] weights[gather[p]] (0 past offsets[E]); weights may be NULL.
+ */
+int oracle_dispatch(const int32_t* ids, const float* weights, int64_t n, int E,
+                    int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
+                    float* sorted_w) {
+    int64_t a, p;
+    int e;
+    int32_t* cursor;
+    if (n < 0 || E <= 0) return 1;
+    for (e = 0; e < E; ++e) counts[e] = 0;
+    for (a = 0; a < n; ++a)
+        if (ids[a] >= 0 && ids[a] < E) counts[ids[a]] += 1;
+    offsets[0] = 0;
+    for (e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    if (!cursor) return 2;
+    for (e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (p = 0; p < n; ++p) {
+        gather[p] = -1;
+        if (sorted_w) sorted_w[p] = 0.0f;
+    }
+    for (a = 0; a < n; ++a) {
+        const int32_t id = ids[a];
+        if (id < 0 || id >= E) {
+            scatter[a] = -1;
+            continue;
+        }
+        p = cursor[id]++;
+        gather[p] = (int32_t)a;
+        scatter[a] = (int32_t)p;
+        if (sorted_w) sorted_w[p] = weights ? weights[a] : 0.0f;
+    }
+    free(cursor);
+    return 0;
+}
