@@ -49,6 +49,7 @@
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -152,6 +153,46 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, float* topk_weights, int32_t* topk_ids,
                                   void* stream);
+
+/*
+ * Dispatch metadata of a routing result ([ROUTING] section "output format":
+ * the kernel-oriented output of routing data, gather index and scatter index;
+ * the page names them without defining their fields, and the definition
+ * below is this library's).  The num_tokens * top_k assignments, numbered
+ * a = token * top_k + slot, are put in order of expert id, keeping the order
+ * of a among assignments of the same expert (a stable counting sort):
+ *   topk_ids       [num_tokens, top_k] int32, e.g. a routing call's output;
+ *                  ids outside [0, num_experts) are dropped
+ *   topk_weights   [num_tokens, top_k] float32, or NULL when sorted_weights
+ *                  is NULL
+ *   expert_counts  [num_experts] int32: assignments per expert
+ *   expert_offsets [num_experts + 1] int32: start of each expert's run in the
+ *                  sorted order (offsets[num_experts] = valid assignments)
+ *   gather_idx     [num_tokens * top_k] int32: the assignment at each sorted
+ *                  position; -1 past offsets[num_experts]
+ *   scatter_idx    [num_tokens * top_k] int32: the sorted position of each
+ *                  assignment, -1 for a dropped one
+ *   sorted_weights [num_tokens * top_k] float32 or NULL: topk_weights in
+ *                  sorted order; 0 past offsets[num_experts]
+ *   workspace      device scratch of at least
+ *                  route_dispatch_workspace_size(num_tokens, top_k,
+ *                  num_experts) bytes, 4-byte aligned, owned by the caller;
+ *                  its contents are overwritten (calls that share it must not
+ *                  overlap)
+ * All arrays are device memory; every int32/float array 4-byte aligned.
+ * Errors: ROUTE_EINVAL for num_tokens < 0, top_k < 1, num_experts < 1, a null
+ * or misaligned required pointer, sorted_weights without topk_weights, or a
+ * workspace smaller than required; ROUTE_ENOTSUP for num_experts > 1024 or
+ * num_tokens * top_k >= 2^31.  num_tokens == 0 is valid and still writes
+ * zero counts and offsets.
+ */
+size_t route_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts);
+route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* topk_weights,
+                                       int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                                       int32_t* expert_counts, int32_t* expert_offsets,
+                                       int32_t* gather_idx, int32_t* scatter_idx,
+                                       float* sorted_weights, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* route_status_str(route_status_t status);

@@ -26,6 +26,8 @@ EXPORTED = (
     "route_grouped_topk",
     "route_biased_grouped_topk",
     "route_fused_router",
+    "route_dispatch_metadata",
+    "route_dispatch_workspace_size",
     "route_status_str",
 )
 
@@ -52,8 +54,13 @@ def lib() -> ctypes.CDLL:
     L.route_biased_grouped_topk.argtypes = [p, i32, p, i64, i32, i32, i32, i32, i32, p, p, p]
     L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32, p, p,
                                      p]
+    L.route_dispatch_metadata.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p, ctypes.c_size_t,
+                                          p]
+    L.route_dispatch_workspace_size.argtypes = [i64, i32, i32]
+    L.route_dispatch_workspace_size.restype = ctypes.c_size_t
     for name in EXPORTED[:-1]:
-        getattr(L, name).restype = i32
+        if name != "route_dispatch_workspace_size":
+            getattr(L, name).restype = i32
     L.route_status_str.argtypes = [i32]
     L.route_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -190,3 +197,42 @@ def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, 
                                     _stream(hidden_states.device, stream)),
            "route_fused_router")
     return w, ids
+
+
+def route_dispatch_workspace_size(num_tokens, top_k, num_experts) -> int:
+    """Bytes of device workspace route_dispatch_metadata needs (0: invalid shape)."""
+    return int(lib().route_dispatch_workspace_size(num_tokens, top_k, num_experts))
+
+
+def route_dispatch_metadata(topk_ids, num_experts, topk_weights=None, workspace=None,
+                            stream=None):
+    """Expert-sorted dispatch metadata of a routing result: the assignments
+    a = token * top_k + slot in order of expert id (stable), ids outside
+    [0, num_experts) dropped.  Returns (expert_counts [E], expert_offsets
+    [E+1], gather_idx [M*K], scatter_idx [M*K], sorted_weights [M*K] or None),
+    all int32 / float32 tensors on the ids' device.  `workspace` (a uint8
+    tensor of at least route_dispatch_workspace_size bytes) is allocated when
+    not given."""
+    M, K = topk_ids.shape
+    dev = topk_ids.device
+    if topk_ids.dtype != torch.int32:
+        raise ValueError("topk_ids must be int32")
+    if topk_weights is not None and (topk_weights.dtype != torch.float32 or
+                                     tuple(topk_weights.shape) != (M, K)):
+        raise ValueError(f"topk_weights must be float32 of shape ({M}, {K})")
+    need = route_dispatch_workspace_size(M, K, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _need_device(topk_ids, topk_weights, workspace)
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    gather = torch.empty(M * K, dtype=torch.int32, device=dev)
+    scatter = torch.empty(M * K, dtype=torch.int32, device=dev)
+    sw = None if topk_weights is None else torch.empty(M * K, dtype=torch.float32, device=dev)
+    _check(lib().route_dispatch_metadata(_ptr(topk_ids), _ptr(topk_weights), M, K, num_experts,
+                                         _ptr(counts), _ptr(offsets), _ptr(gather),
+                                         _ptr(scatter), _ptr(sw), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(dev, stream)),
+           "route_dispatch_metadata")
+    return counts, offsets, gather, scatter, sw

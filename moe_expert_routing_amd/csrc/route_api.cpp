@@ -106,6 +106,44 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
     return moe_route::launch_fused_router(f);
 }
 
+size_t route_dispatch_workspace_size(int64_t num_tokens, int32_t top_k, int32_t num_experts) {
+    if (num_tokens < 0 || top_k < 1 || num_experts < 1 || num_experts > moe_route::kMaxExperts)
+        return 0;
+    const int64_t n = num_tokens * top_k;
+    if (n >= (int64_t(1) << 31)) return 0;
+    return moe_route::dispatch_workspace_bytes(n, num_experts);
+}
+
+route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* topk_weights,
+                                       int64_t num_tokens, int32_t top_k, int32_t num_experts,
+                                       int32_t* expert_counts, int32_t* expert_offsets,
+                                       int32_t* gather_idx, int32_t* scatter_idx,
+                                       float* sorted_weights, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (num_tokens < 0 || top_k < 1 || num_experts < 1) return ROUTE_EINVAL;
+    if (num_experts > moe_route::kMaxExperts) return ROUTE_ENOTSUP;
+    if (num_tokens > (int64_t(1) << 31) / top_k ||
+        num_tokens * top_k >= (int64_t(1) << 31)) return ROUTE_ENOTSUP;
+    const int64_t n = num_tokens * top_k;
+    if (!expert_counts || !expert_offsets || !workspace) return ROUTE_EINVAL;
+    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(workspace, 4))
+        return ROUTE_EINVAL;
+    if (workspace_bytes < moe_route::dispatch_workspace_bytes(n, num_experts)) return ROUTE_EINVAL;
+    if (sorted_weights && !topk_weights) return ROUTE_EINVAL;
+    if (n > 0) {
+        if (!topk_ids || !gather_idx || !scatter_idx) return ROUTE_EINVAL;
+        if (!aligned(topk_ids, 4) || !aligned(gather_idx, 4) || !aligned(scatter_idx, 4))
+            return ROUTE_EINVAL;
+        if (sorted_weights && (!aligned(sorted_weights, 4) || !aligned(topk_weights, 4)))
+            return ROUTE_EINVAL;
+    }
+    moe_route::DispatchProblem d{topk_ids, sorted_weights ? topk_weights : nullptr, n,
+                                 num_experts, expert_counts, expert_offsets, gather_idx,
+                                 scatter_idx, sorted_weights, workspace,
+                                 static_cast<hipStream_t>(stream)};
+    return moe_route::launch_dispatch(d);
+}
+
 const char* route_status_str(route_status_t status) {
     switch (status) {
         case ROUTE_OK: return "ROUTE_OK";

@@ -31,6 +31,21 @@ struct FusedProblem {
     RouteProblem route;     // logits/dtype unused
 };
 
+// Dispatch metadata of a routing result (route_dispatch.hip).
+struct DispatchProblem {
+    const int32_t* ids;     // [n] expert ids (n = M * K)
+    const float* weights;   // [n] or nullptr when sorted_weights is nullptr
+    int64_t n;
+    int E;
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E + 1]
+    int32_t* gather;        // [n]
+    int32_t* scatter;       // [n]
+    float* sorted_weights;  // [n] or nullptr
+    void* workspace;        // dispatch_workspace_bytes(n, E)
+    hipStream_t stream;
+};
+
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 64;
@@ -40,5 +55,7 @@ constexpr int kMaxGroups = 64;
 route_status_t launch_route(const RouteProblem& p);
 route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
+size_t dispatch_workspace_bytes(int64_t n, int E);
+route_status_t launch_dispatch(const DispatchProblem& d);
 
 }  // namespace moe_route

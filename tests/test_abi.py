@@ -113,3 +113,50 @@ def test_binding_has_no_cpu_fallback():
         mr.route_topk_softmax(x, 2)
     with pytest.raises(ValueError, match="must live on the GPU"):
         mr.route_biased_grouped_topk(x.bfloat16(), torch.zeros(8), 2, 2, 1)
+
+
+def test_dispatch_workspace_size():
+    ws = mr.lib().route_dispatch_workspace_size
+    assert ws(-1, 8, 256) == 0
+    assert ws(10, 0, 256) == 0
+    assert ws(10, 8, 0) == 0
+    assert ws(10, 8, 2048) == 0
+    assert ws(1 << 28, 8, 256) == 0                      # M*K beyond 2^31
+    # int32 counts per (expert, chunk of 512 assignments) plus per-expert totals
+    assert ws(65536, 8, 256) == 4 * 256 * (1024 + 1)
+    assert ws(0, 8, 256) == 4 * 256
+    assert ws(3, 2, 8) == 4 * 8 * 2
+
+
+def disp(M=4, K=8, E=256, ids=P, w=NULL, counts=Q, offsets=R, gather=P, scatter=Q, sw=NULL,
+         ws=R, wsb=1 << 20):
+    return mr.lib().route_dispatch_metadata(ids, w, M, K, E, counts, offsets, gather, scatter,
+                                            sw, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), mr.ROUTE_EINVAL),
+    (dict(K=0), mr.ROUTE_EINVAL),
+    (dict(E=0), mr.ROUTE_EINVAL),
+    (dict(E=1025), mr.ROUTE_ENOTSUP),
+    (dict(M=1 << 28), mr.ROUTE_ENOTSUP),
+    (dict(ids=NULL), mr.ROUTE_EINVAL),
+    (dict(counts=NULL), mr.ROUTE_EINVAL),
+    (dict(offsets=NULL), mr.ROUTE_EINVAL),
+    (dict(gather=NULL), mr.ROUTE_EINVAL),
+    (dict(scatter=NULL), mr.ROUTE_EINVAL),
+    (dict(ws=NULL), mr.ROUTE_EINVAL),
+    (dict(wsb=4 * 256), mr.ROUTE_EINVAL),                  # workspace too small
+    (dict(sw=P), mr.ROUTE_EINVAL),                         # sorted weights need weights
+    (dict(ids=ctypes.c_void_p(0x10002)), mr.ROUTE_EINVAL),  # misaligned
+    (dict(counts=ctypes.c_void_p(0x20001)), mr.ROUTE_EINVAL),
+])
+def test_dispatch_validation(kw, code):
+    assert disp(**kw) == code
+
+
+def test_dispatch_binding_has_no_cpu_fallback():
+    import torch
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        mr.route_dispatch_metadata(torch.zeros(2, 2, dtype=torch.int32), 4,
+                                   workspace=torch.zeros(64, dtype=torch.uint8))

@@ -1,0 +1,93 @@
+"""GPU parity of route_dispatch_metadata (expert-sorted dispatch metadata)
+against the oracle's stable counting sort: integer outputs bit-exact, sorted
+weights exact copies."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_routing_amd as mr
+import oracle
+from gpu_util import log, to_device
+from workloads import WORKLOADS, make_bias, make_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(ids_np, E, w_np=None, workspace=None):
+    ids_t = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).cuda()
+    w_t = None if w_np is None else torch.from_numpy(np.ascontiguousarray(w_np)).cuda()
+    c, o, g, s, sw = mr.route_dispatch_metadata(ids_t, E, w_t, workspace=workspace)
+    torch.cuda.synchronize()
+    rc, ro, rg, rs, rsw = oracle.dispatch(ids_np, E, w_np)
+    np.testing.assert_array_equal(c.cpu().numpy(), rc)
+    np.testing.assert_array_equal(o.cpu().numpy(), ro)
+    np.testing.assert_array_equal(g.cpu().numpy(), rg)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    if w_np is not None:
+        np.testing.assert_array_equal(sw.cpu().numpy(), rsw)
+    return c, o, g, s, sw
+
+
+@pytest.mark.parametrize("M,K,E,lo,hi,seed", [
+    (1, 1, 1, 0, 1, 0),          # a single assignment
+    (3, 2, 4, -1, 6, 1),         # dropped ids on both sides
+    (37, 3, 8, 0, 8, 2),         # fewer than one 64-lane step
+    (1000, 6, 160, -3, 170, 3),  # ragged chunks, some dropped
+    (4096, 8, 256, 0, 256, 4),   # whole 512-assignment chunks
+    (513, 1, 1024, -5, 1024, 5), # widest expert id (11 bits)
+    (20000, 2, 1, -1, 1, 6),     # one expert, half the ids dropped
+])
+def test_dispatch_random_ids(M, K, E, lo, hi, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(lo, hi, size=(M, K)).astype(np.int32)
+    w = rng.random((M, K), dtype=np.float32)
+    log(f"[gpu] dispatch random M={M} K={K} E={E} ids in [{lo},{hi})")
+    _compare(ids, E, w)
+    _compare(ids, E)  # without weights
+
+
+def test_dispatch_of_full_size_routing_output():
+    """Route the 65536-token biased grouped workload on the GPU, then dispatch
+    its ids; the oracle sorts the same ids."""
+    wl = WORKLOADS["biased_grouped_e256"]
+    x, b = make_logits(wl), make_bias(wl)
+    log("[gpu] dispatch of route_biased_grouped_topk output, M=65536 E=256 K=8")
+    w, ids = mr.route_biased_grouped_topk(to_device(x), to_device(b), wl.K, wl.G, wl.TG, True)
+    torch.cuda.synchronize()
+    c, o, g, s, sw = _compare(ids.cpu().numpy(), wl.E, w.cpu().numpy())
+    assert int(c.sum()) == 65536 * 8
+
+
+def test_dispatch_all_to_one_expert():
+    """One expert takes every assignment: one run across every chunk."""
+    ids = np.full((8192, 8), 5, np.int32)
+    log("[gpu] dispatch all ids = 5")
+    _compare(ids, 256, np.arange(8192 * 8, dtype=np.float32).reshape(8192, 8))
+
+
+def test_dispatch_empty():
+    ids = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    c, o, g, s, sw = mr.route_dispatch_metadata(ids, 16)
+    torch.cuda.synchronize()
+    assert (c.cpu() == 0).all() and (o.cpu() == 0).all() and g.numel() == 0
+
+
+def test_dispatch_reuses_workspace_and_is_deterministic():
+    rng = np.random.default_rng(9)
+    ws = torch.empty(mr.route_dispatch_workspace_size(5000, 8, 256), dtype=torch.uint8,
+                     device="cuda")
+    big = rng.integers(0, 256, size=(5000, 8)).astype(np.int32)
+    small = rng.integers(0, 256, size=(700, 8)).astype(np.int32)
+    log("[gpu] dispatch workspace reuse")
+    a = _compare(big, 256, workspace=ws)
+    _compare(small, 256, workspace=ws)
+    b = _compare(big, 256, workspace=ws)
+    for x, y in zip(a[:4], b[:4]):
+        assert torch.equal(x, y)
+
+
+def test_dispatch_rejects_small_workspace():
+    ids = torch.zeros((100, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        mr.route_dispatch_metadata(ids, 256, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                   device="cuda"))
