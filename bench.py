@@ -215,6 +215,29 @@ def measure_all(out_path=None):
          "frac_mfma_bf16_kernel": flops / (kern * 1e-6) / 2.5e15}
     results.append(r)
     eprint(json.dumps(r))
+    # dispatch metadata of the 65536-token biased grouped routing output
+    wl = WORKLOADS["biased_grouped_e256"]
+    xb = dev_tensor(make_logits(wl))
+    bb = dev_tensor(make_bias(wl))
+    rw, rids = mr.route_biased_grouped_topk(xb, bb, wl.K, wl.G, wl.TG, wl.renormalize)
+    n_sets = 8
+    ids_sets = [rids] + [rids.clone() for _ in range(n_sets - 1)]
+    w_sets = [rw] + [rw.clone() for _ in range(n_sets - 1)]
+    ws = torch.empty(mr.route_dispatch_workspace_size(wl.M, wl.K, wl.E), dtype=torch.uint8,
+                     device=dev)
+
+    def launch_disp(i):
+        mr.route_dispatch_metadata(ids_sets[i], wl.E, w_sets[i], workspace=ws, stream=stream)
+    per_call, kern = time_calls(launch_disp, n_sets, stream, steps=200, warmup=20)
+    n = wl.M * wl.K
+    nbytes = 2 * n * 4 + n * 4 + 3 * n * 4 + 2 * wl.E * 4  # ids twice, weights; 3 outputs
+    r = {"workload": "dispatch_metadata_e256_m65536", "entry": "route_dispatch_metadata",
+         "M": wl.M, "K": wl.K, "E": wl.E, "rotating_sets": n_sets, "us_per_call": per_call,
+         "kernel_us": kern, "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
+         "note": "three kernels per call; us_per_call includes the library's allocations "
+                 "of the outputs in the Python binding"}
+    results.append(r)
+    eprint(json.dumps(r))
     if out_path:
         with open(out_path, "w") as f:
             json.dump(results, f, indent=1)

@@ -9,17 +9,21 @@
 // weights in sorted order.  Ids outside [0, E) are dropped.
 //
 // Three kernels, all on the caller's stream, with a caller-provided
-// workspace cnt[E][W] + totals[E] (W = chunks of kChunk assignments):
-//   1. hist:  each wave counts its chunk's assignments per expert (LDS
-//             atomics in a wave-private histogram) into cnt[e][w];
-//   2. scan:  one wave per expert turns cnt[e][*] into exclusive offsets
-//             across chunks and writes the expert's total;
-//   3. place: every block scans the totals into expert offsets; each wave
-//             walks its chunk 64 assignments at a time.  Lanes with the same
-//             expert find each other with one ballot per bit of the expert
-//             id; a lane's rank among them (mbcnt) plus the expert's running
-//             cursor (wave-private LDS) is its sorted position, so equal ids
-//             keep their order without ordered atomics.
+// workspace cnt[B][E] + totals[E] (B = blocks of kBlockChunk assignments):
+//   1. hist:  each block counts its chunk per expert (LDS atomics) into its
+//             row cnt[b][*];
+//   2. scan:  64 experts per block, each column cnt[*][e] split over 16
+//             segments, turns each column into exclusive offsets across
+//             blocks and writes the expert's total;
+//   3. place: each block scans the totals into expert offsets (block 0 also
+//             writes counts and offsets), recounts its chunk per wave, so that every wave
+//             starts from its own cursor per expert (the expert offset plus
+//             the counts of earlier blocks and earlier waves), then walks its
+//             part 64 assignments at a time.  Lanes with the same expert find
+//             each other with one ballot per bit of the expert id; a lane's
+//             rank among them (mbcnt) plus its wave's cursor is its sorted
+//             position, so equal ids keep their order without ordered
+//             atomics.
 #include <hip/hip_runtime.h>
 
 #include "route_common.cuh"
@@ -28,74 +32,119 @@
 namespace moe_route {
 namespace {
 
-constexpr int kChunk = 512;  // assignments per wave chunk
 constexpr int kDispWaves = 4;
 constexpr int kDispThreads = kDispWaves * kWave;
+constexpr int kPerLane = 8;                              // assignments per lane
+constexpr int kWaveChunk = kPerLane * kWave;             // 512 per wave
+constexpr int kBlockChunk = kDispWaves * kWaveChunk;     // 2048 per block
+constexpr int kScanThreads = 1024;                       // >= max experts
+constexpr int kScanBatch = 16;                           // loads in flight per thread
 
 __device__ __forceinline__ bool valid_id(int32_t id, int E) { return id >= 0 && id < E; }
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int W, int32_t* __restrict__ cnt) {
-    extern __shared__ int32_t s_hist[];  // [kDispWaves][E]
-    const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
-    const int w = blockIdx.x * kDispWaves + wv;
-    if (w >= W) return;  // no block-wide barrier in this kernel
-    int32_t* h = s_hist + wv * E;
-    for (int e = lane; e < E; e += kWave) h[e] = 0;
-    // A wave's LDS operations complete in order: the zeros land before the
-    // increments, the increments before the reads below.
-    const int64_t a0 = (int64_t)w * kChunk;
-    const int64_t a1 = min(a0 + kChunk, n);
-    for (int64_t a = a0 + lane; a < a1; a += kWave) {
-        const int32_t id = ids[a];
-        if (valid_id(id, E)) atomicAdd(&h[id], 1);
+    const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ cnt) {
+    extern __shared__ int32_t s_hist[];  // [E]
+    const int t = threadIdx.x;
+    const int64_t a0 = (int64_t)blockIdx.x * kBlockChunk + t;
+    int32_t idv[kPerLane];  // all loads in flight at once
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int64_t a = a0 + (int64_t)j * kDispThreads;
+        idv[j] = a < n ? ids[a] : -1;
     }
-    for (int e = lane; e < E; e += kWave) cnt[(int64_t)e * W + w] = h[e];
+    for (int e = t; e < E; e += kDispThreads) s_hist[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        if (valid_id(idv[j], E)) atomicAdd(&s_hist[idv[j]], 1);
+    __syncthreads();
+    for (int e = t; e < E; e += kDispThreads) cnt[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
-__global__ __launch_bounds__(kWave) void dispatch_scan_kernel(int W, int32_t* __restrict__ cnt,
-                                                              int32_t* __restrict__ totals) {
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x;
-    int32_t* row = cnt + (int64_t)e * W;
-    const int per = (W + kWave - 1) / kWave;
-    const int b0 = min(lane * per, W), b1 = min(b0 + per, W);
-    int sum = 0;
-    for (int i = b0; i < b1; ++i) sum += row[i];
-    int incl = sum;
+// Block x, thread t: expert e = 64 x + t % 64 over segment t / 64 of the
+// block rows.  Segments combine in LDS; each column is rewritten as exclusive
+// offsets across blocks and the expert's total is written.
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    int E, int B, int32_t* __restrict__ cnt, int32_t* __restrict__ totals) {
+    constexpr int S = kScanThreads / kWave;  // 16 segments
+    __shared__ int32_t s_part[S][kWave];
+    const int t = threadIdx.x;
+    const int lane = t % kWave, seg = t / kWave;
+    const int e = blockIdx.x * kWave + lane;
+    const bool active = e < E;
+    const int per = (B + S - 1) / S;
+    const int b0 = min(seg * per, B), b1 = min(b0 + per, B);
+    int part = 0;
+    for (int b = b0; b < b1; b += kScanBatch) {
+        int v[kScanBatch];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += v;
+        for (int i = 0; i < kScanBatch; ++i)
+            v[i] = (active && b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i) part += v[i];
     }
-    int run = incl - sum;
-    for (int i = b0; i < b1; ++i) {
-        const int c = row[i];
-        row[i] = run;
-        run += c;
+    s_part[seg][lane] = part;
+    __syncthreads();
+    int start = 0, total = 0;
+    for (int q = 0; q < S; ++q) {
+        const int v = s_part[q][lane];
+        if (q < seg) start += v;
+        total += v;
     }
-    if (lane == kWave - 1) totals[e] = incl;
+    if (active) {
+        for (int b = b0; b < b1; b += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i)
+                v[i] = (b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) {
+                if (b + i < b1) cnt[(int64_t)(b + i) * E + e] = start;
+                start += v[i];
+            }
+        }
+        if (seg == 0) totals[e] = total;
+    }
 }
 
 __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t n, int E, int W,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t n, int E,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ gather,
     int32_t* __restrict__ scatter, float* __restrict__ sorted_w) {
     extern __shared__ int32_t smem[];
-    int32_t* s_off = smem;               // [E + 1] expert offsets
-    int32_t* s_wsum = smem + E + 1;      // [kDispWaves] scan carries
-    int32_t* s_run = s_wsum + kDispWaves;  // [kDispWaves][E] running cursors
+    int32_t* s_off = smem;                     // [E + 1] expert offsets
+    int32_t* s_wsum = s_off + E + 1;           // [kDispWaves] scan carries
+    int32_t* s_cur = s_wsum + kDispWaves;      // [kDispWaves][E] counts, then cursors
+    constexpr int kEPT = kMaxExperts / kDispThreads;  // experts per thread (<= 4)
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wv = t / kWave;
-
+    // every global load of the block goes out first: this lane's assignments
+    // a0 + 64 j, the expert totals (experts kEPT t ..), the block's row of
+    // offsets across blocks
+    const int64_t a0 = (int64_t)blockIdx.x * kBlockChunk + (int64_t)wv * kWaveChunk + lane;
+    int32_t idv[kPerLane];
+    float wv8[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int64_t a = a0 + (int64_t)j * kWave;
+        idv[j] = a < n ? ids[a] : -1;
+        wv8[j] = (sorted_w && a < n) ? wts[a] : 0.0f;
+    }
+    const int32_t* row = cnt + (int64_t)blockIdx.x * E;
+    int tot[kEPT], rowv[kEPT];
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) {
+        const int e = kEPT * t + i;
+        tot[i] = e < E ? totals[e] : 0;
+        rowv[i] = e < E ? row[e] : 0;
+    }
     // expert offsets: exclusive scan of the totals over the block
-    const int per = (E + kDispThreads - 1) / kDispThreads;
-    const int e0 = min(t * per, E), e1 = min(e0 + per, E);
     int sum = 0;
-    for (int e = e0; e < e1; ++e) sum += totals[e];
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) sum += tot[i];
     int incl = sum;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -103,20 +152,30 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         if (lane >= o) incl += v;
     }
     if (lane == kWave - 1) s_wsum[wv] = incl;
+    for (int i = t; i < kDispWaves * E; i += kDispThreads) s_cur[i] = 0;
     __syncthreads();
-    int carry = 0;
-    for (int q = 0; q < wv; ++q) carry += s_wsum[q];
-    int run = carry + incl - sum;
-    for (int e = e0; e < e1; ++e) {
-        s_off[e] = run;
-        run += totals[e];
+    int run = incl - sum;
+    for (int q = 0; q < wv; ++q) run += s_wsum[q];
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) {
+        const int e = kEPT * t + i;
+        if (e < E) s_off[e] = run;
+        run += tot[i];
     }
-    if (t == kDispThreads - 1) s_off[E] = carry + incl;
+    if (t == kDispThreads - 1) s_off[E] = run;
+    int32_t* cur = s_cur + wv * E;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+        if (valid_id(idv[j], E)) atomicAdd(&cur[idv[j]], 1);
     __syncthreads();
     if (blockIdx.x == 0) {
-        for (int e = t; e < E; e += kDispThreads) {
-            counts[e] = totals[e];
-            offsets[e] = s_off[e];
+#pragma unroll
+        for (int i = 0; i < kEPT; ++i) {
+            const int e = kEPT * t + i;
+            if (e < E) {
+                counts[e] = tot[i];
+                offsets[e] = s_off[e];
+            }
         }
         if (t == 0) offsets[E] = s_off[E];
     }
@@ -127,21 +186,29 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         gather[p] = -1;
         if (sorted_w) sorted_w[p] = 0.0f;
     }
-
-    const int w = blockIdx.x * kDispWaves + wv;
-    if (w >= W) return;  // no block-wide barrier below
-    int32_t* cur = s_run + wv * E;
-    for (int e = lane; e < E; e += kWave) cur[e] = s_off[e] + cnt[(int64_t)e * W + w];
+    // cursor of wave q for expert e: expert offset + earlier blocks + earlier waves
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) {
+        const int e = kEPT * t + i;
+        if (e < E) {
+            int c = s_off[e] + rowv[i];
+#pragma unroll
+            for (int q = 0; q < kDispWaves; ++q) {
+                const int v = s_cur[q * E + e];
+                s_cur[q * E + e] = c;
+                c += v;
+            }
+        }
+    }
+    __syncthreads();
     // expert ids need nb bits; the all-ones pattern of nb bits is >= E and
     // tags dropped or absent assignments
     const int nb = 32 - __clz(E);
     const uint32_t none = (1u << nb) - 1u;
-    const int64_t a0 = (int64_t)w * kChunk;
-    const int64_t a1 = min(a0 + kChunk, n);
-    for (int64_t base = a0; base < a1; base += kWave) {
-        const int64_t a = base + lane;
-        const bool in = a < a1;
-        const int32_t id = in ? ids[a] : -1;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+        const int64_t a = a0 + (int64_t)j * kWave;
+        const int32_t id = idv[j];
         const bool ok = valid_id(id, E);
         const uint32_t key = ok ? static_cast<uint32_t>(id) : none;
         uint64_t same = ~0ull;  // lanes whose key equals this lane's
@@ -159,9 +226,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
             const int32_t p = start + rank;
             gather[p] = static_cast<int32_t>(a);
             scatter[a] = p;
-            if (sorted_w) sorted_w[p] = wts[a];
+            if (sorted_w) sorted_w[p] = wv8[j];
             if (rank == size - 1) cur[id] = start + size;  // one writer per expert
-        } else if (in) {
+        } else if (a < n) {
             scatter[a] = -1;
         }
     }
@@ -170,24 +237,24 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
 }  // namespace
 
 size_t dispatch_workspace_bytes(int64_t n, int E) {
-    const int64_t W = (n + kChunk - 1) / kChunk;
-    return sizeof(int32_t) * static_cast<size_t>(E) * static_cast<size_t>(W + 1);
+    const int64_t B = (n + kBlockChunk - 1) / kBlockChunk;
+    return sizeof(int32_t) * static_cast<size_t>(E) * static_cast<size_t>(B + 1);
 }
 
 route_status_t launch_dispatch(const DispatchProblem& d) {
-    const int64_t W64 = (d.n + kChunk - 1) / kChunk;
-    const int W = static_cast<int>(W64);
+    const int B = static_cast<int>((d.n + kBlockChunk - 1) / kBlockChunk);
     int32_t* cnt = static_cast<int32_t*>(d.workspace);
-    int32_t* totals = cnt + static_cast<int64_t>(d.E) * W;
-    const int blocks = W > 0 ? (W + kDispWaves - 1) / kDispWaves : 1;
-    if (W > 0) {
-        hipLaunchKernelGGL(dispatch_hist_kernel, dim3(blocks), dim3(kDispThreads),
-                           sizeof(int32_t) * kDispWaves * d.E, d.stream, d.ids, d.n, d.E, W, cnt);
+    int32_t* totals = cnt + static_cast<int64_t>(d.E) * B;
+    static_assert(kMaxExperts % kDispThreads == 0, "experts per place thread");
+    if (B > 0) {
+        hipLaunchKernelGGL(dispatch_hist_kernel, dim3(B), dim3(kDispThreads),
+                           sizeof(int32_t) * d.E, d.stream, d.ids, d.n, d.E, cnt);
     }
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(d.E), dim3(kWave), 0, d.stream, W, cnt, totals);
-    hipLaunchKernelGGL(dispatch_place_kernel, dim3(blocks), dim3(kDispThreads),
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3((d.E + kWave - 1) / kWave), dim3(kScanThreads),
+                       0, d.stream, d.E, B, cnt, totals);
+    hipLaunchKernelGGL(dispatch_place_kernel, dim3(B > 0 ? B : 1), dim3(kDispThreads),
                        sizeof(int32_t) * (d.E + 1 + kDispWaves + kDispWaves * d.E), d.stream,
-                       d.ids, d.weights, d.n, d.E, W, cnt, totals, d.counts, d.offsets, d.gather,
+                       d.ids, d.weights, d.n, d.E, cnt, totals, d.counts, d.offsets, d.gather,
                        d.scatter, d.sorted_weights);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }

@@ -122,8 +122,8 @@ def test_dispatch_workspace_size():
     assert ws(10, 8, 0) == 0
     assert ws(10, 8, 2048) == 0
     assert ws(1 << 28, 8, 256) == 0                      # M*K beyond 2^31
-    # int32 counts per (expert, chunk of 512 assignments) plus per-expert totals
-    assert ws(65536, 8, 256) == 4 * 256 * (1024 + 1)
+    # int32 counts per (block of 2048 assignments, expert) plus per-expert totals
+    assert ws(65536, 8, 256) == 4 * 256 * (256 + 1)
     assert ws(0, 8, 256) == 4 * 256
     assert ws(3, 2, 8) == 4 * 8 * 2
 
