@@ -56,6 +56,10 @@ def _load():
         lib.oracle_router_logits.restype = i32
         lib.oracle_dispatch.argtypes = [p, p, i64, i32, p, p, p, p, p]
         lib.oracle_dispatch.restype = i32
+        lib.oracle_fuse_shared_expert.argtypes = [p, p, i64, i32, p, ctypes.c_double]
+        lib.oracle_fuse_shared_expert.restype = i32
+        lib.oracle_sort_ids.argtypes = [p, p, i64, i32]
+        lib.oracle_sort_ids.restype = i32
         _lib = lib
     return _lib
 
@@ -157,3 +161,31 @@ def dispatch(topk_ids, num_experts, topk_weights=None):
     if rc != 0:
         raise ValueError(f"oracle_dispatch rejected its arguments (code {rc})")
     return counts, offsets, gather, scatter, sw
+
+
+def fuse_shared_expert(topk_weights, topk_ids, shared_ids, routed_scaling_factor=None):
+    """The shared-expert slot: returns copies of (weights, ids) whose last slot
+    holds shared_ids[m] and, when routed_scaling_factor is given, the sum of
+    the row's other weights divided by it."""
+    w = np.array(topk_weights, dtype=np.float32, copy=True, order="C")
+    ids = np.array(topk_ids, dtype=np.int32, copy=True, order="C")
+    sid = np.ascontiguousarray(shared_ids, dtype=np.int32).reshape(-1)
+    M, K = ids.shape
+    if sid.size != M:
+        raise ValueError("shared_ids needs one id per token")
+    rsf = 0.0 if routed_scaling_factor is None else float(routed_scaling_factor)
+    rc = _load().oracle_fuse_shared_expert(_ptr(w), _ptr(ids), M, K, _ptr(sid), rsf)
+    if rc != 0:
+        raise ValueError(f"oracle_fuse_shared_expert rejected its arguments (code {rc})")
+    return w, ids
+
+
+def sort_ids(topk_weights, topk_ids):
+    """Copies of (weights, ids) with each row's pairs in ascending id order."""
+    w = np.array(topk_weights, dtype=np.float32, copy=True, order="C")
+    ids = np.array(topk_ids, dtype=np.int32, copy=True, order="C")
+    M, K = ids.shape
+    rc = _load().oracle_sort_ids(_ptr(w), _ptr(ids), M, K)
+    if rc != 0:
+        raise ValueError(f"oracle_sort_ids rejected its arguments (code {rc})")
+    return w, ids

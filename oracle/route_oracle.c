@@ -313,3 +313,56 @@ int oracle_dispatch(const int32_t* ids, const float* weights, int64_t n, int E,
     free(cursor);
     return 0;
 }
+
+/*
+ * Shared-expert slot ([ROUTING] section 6): with fused shared experts the
+ * last of a row's K slots is handed to a shared expert.  The page draws its
+ * id at random from [E, E + num_shared); here the draw is an input
+ * (shared_ids[m]), so that the result is reproducible.  When a routed
+ * scaling factor is given (rsf != 0), the slot's weight becomes the sum of
+ * the row's other K-1 weights divided by it; otherwise the weight is left as
+ * it was.  The other slots are untouched.  Applied in place.
+ */
+int oracle_fuse_shared_expert(float* weights, int32_t* ids, int64_t M, int K,
+                              const int32_t* shared_ids, double rsf) {
+    int64_t m;
+    int k;
+    if (M < 0 || K < 2) return 1;
+    for (m = 0; m < M; ++m) {
+        ids[m * K + (K - 1)] = shared_ids[m];
+        if (rsf != 0.0) {
+            double s = 0.0;
+            for (k = 0; k < K - 1; ++k) s += (double)weights[m * K + k];
+            weights[m * K + (K - 1)] = (float)(s / rsf);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Ascending id order: each row's K (id, weight) pairs reordered by expert id,
+ * lowest first (equal ids keep their slot order).  Routing emits ids in score
+ * order; some consumers want them by expert, as the page on MiniMax-M3's
+ * decode top-k ("[sglang] MiniMax-M3 ... FP8 Attention GEMM", section 1)
+ * orders its block ids.  Applied in place; insertion sort per row.
+ */
+int oracle_sort_ids(float* weights, int32_t* ids, int64_t M, int K) {
+    int64_t m;
+    int i, j;
+    if (M < 0 || K < 1) return 1;
+    for (m = 0; m < M; ++m) {
+        float* w = weights + m * K;
+        int32_t* d = ids + m * K;
+        for (i = 1; i < K; ++i) {
+            const int32_t di = d[i];
+            const float wi = w[i];
+            for (j = i - 1; j >= 0 && d[j] > di; --j) {
+                d[j + 1] = d[j];
+                w[j + 1] = w[j];
+            }
+            d[j + 1] = di;
+            w[j + 1] = wi;
+        }
+    }
+    return 0;
+}
