@@ -194,6 +194,38 @@ route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* top
                                        float* sorted_weights, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * Shared-expert slot ([ROUTING] section 6), in place on a routing result:
+ * row m's last slot gets topk_ids[m][top_k-1] = shared_expert_ids[m] (the
+ * page draws this id at random from [E, E + num_shared); the caller supplies
+ * the draw).  When routed_scaling_factor != 0 the slot's weight becomes the
+ * sum of the row's other top_k - 1 weights divided by it (fp32 sum in slot
+ * order, IEEE division); with 0 the weight is left as it is.  Other slots are
+ * untouched.
+ *   topk_weights [num_tokens, top_k] float32, topk_ids [num_tokens, top_k]
+ *   int32, shared_expert_ids [num_tokens] int32; device memory, 4-byte
+ *   aligned.
+ * Errors: ROUTE_EINVAL for num_tokens < 0, top_k < 2, a NaN or infinite
+ * factor, or a null or misaligned pointer (num_tokens > 0); ROUTE_ENOTSUP for
+ * top_k > 64.  num_tokens == 0 returns ROUTE_OK without touching the GPU.
+ */
+route_status_t route_fuse_shared_expert(float* topk_weights, int32_t* topk_ids,
+                                        int64_t num_tokens, int32_t top_k,
+                                        const int32_t* shared_expert_ids,
+                                        float routed_scaling_factor, void* stream);
+
+/*
+ * Ascending id order, in place on a routing result: each row's top_k
+ * (id, weight) pairs reordered by expert id, lowest first; equal ids keep
+ * their slot order.  (Routing emits ids by selection score; some consumers
+ * want them by expert, as the decode top-k of "[sglang] MiniMax-M3 ... FP8
+ * Attention GEMM", section 1, orders its ids.)
+ * Errors: ROUTE_EINVAL for num_tokens < 0, top_k < 1, or a null or
+ * misaligned pointer (num_tokens > 0); ROUTE_ENOTSUP for top_k > 64.
+ */
+route_status_t route_sort_ids(float* topk_weights, int32_t* topk_ids, int64_t num_tokens,
+                              int32_t top_k, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* route_status_str(route_status_t status);
 

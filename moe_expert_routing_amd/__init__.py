@@ -28,6 +28,8 @@ EXPORTED = (
     "route_fused_router",
     "route_dispatch_metadata",
     "route_dispatch_workspace_size",
+    "route_fuse_shared_expert",
+    "route_sort_ids",
     "route_status_str",
 )
 
@@ -57,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.route_dispatch_metadata.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p, ctypes.c_size_t,
                                           p]
     L.route_dispatch_workspace_size.argtypes = [i64, i32, i32]
+    L.route_fuse_shared_expert.argtypes = [p, p, i64, i32, p, ctypes.c_float, p]
+    L.route_sort_ids.argtypes = [p, p, i64, i32, p]
     L.route_dispatch_workspace_size.restype = ctypes.c_size_t
     for name in EXPORTED[:-1]:
         if name != "route_dispatch_workspace_size":
@@ -236,3 +240,33 @@ def route_dispatch_metadata(topk_ids, num_experts, topk_weights=None, workspace=
                                          _stream(dev, stream)),
            "route_dispatch_metadata")
     return counts, offsets, gather, scatter, sw
+
+
+def route_fuse_shared_expert(topk_weights, topk_ids, shared_expert_ids,
+                             routed_scaling_factor=None, stream=None):
+    """In place: each row's last slot gets its shared-expert id and, with a
+    routed scaling factor, the sum of the row's other weights divided by it.
+    Returns (topk_weights, topk_ids)."""
+    M, K = topk_ids.shape
+    if topk_weights.dtype != torch.float32 or topk_ids.dtype != torch.int32:
+        raise ValueError("topk_weights must be float32 and topk_ids int32")
+    if shared_expert_ids.dtype != torch.int32 or shared_expert_ids.numel() != M:
+        raise ValueError(f"shared_expert_ids must be int32 with {M} entries")
+    _need_device(topk_weights, topk_ids, shared_expert_ids)
+    rsf = 0.0 if routed_scaling_factor is None else float(routed_scaling_factor)
+    _check(lib().route_fuse_shared_expert(_ptr(topk_weights), _ptr(topk_ids), M, K,
+                                          _ptr(shared_expert_ids), rsf,
+                                          _stream(topk_ids.device, stream)),
+           "route_fuse_shared_expert")
+    return topk_weights, topk_ids
+
+
+def route_sort_ids(topk_weights, topk_ids, stream=None):
+    """In place: each row's (id, weight) pairs in ascending id order."""
+    M, K = topk_ids.shape
+    if topk_weights.dtype != torch.float32 or topk_ids.dtype != torch.int32:
+        raise ValueError("topk_weights must be float32 and topk_ids int32")
+    _need_device(topk_weights, topk_ids)
+    _check(lib().route_sort_ids(_ptr(topk_weights), _ptr(topk_ids), M, K,
+                                _stream(topk_ids.device, stream)), "route_sort_ids")
+    return topk_weights, topk_ids

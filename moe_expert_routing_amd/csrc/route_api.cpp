@@ -144,6 +144,35 @@ route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* top
     return moe_route::launch_dispatch(d);
 }
 
+route_status_t route_fuse_shared_expert(float* topk_weights, int32_t* topk_ids,
+                                        int64_t num_tokens, int32_t top_k,
+                                        const int32_t* shared_expert_ids,
+                                        float routed_scaling_factor, void* stream) {
+    if (num_tokens < 0 || top_k < 2) return ROUTE_EINVAL;
+    if (!(routed_scaling_factor == routed_scaling_factor) ||
+        routed_scaling_factor - routed_scaling_factor != 0.0f)  // NaN or infinite
+        return ROUTE_EINVAL;
+    if (top_k > moe_route::kMaxTopK) return ROUTE_ENOTSUP;
+    if (num_tokens == 0) return ROUTE_OK;
+    if (!topk_weights || !topk_ids || !shared_expert_ids) return ROUTE_EINVAL;
+    if (!aligned(topk_weights, 4) || !aligned(topk_ids, 4) || !aligned(shared_expert_ids, 4))
+        return ROUTE_EINVAL;
+    return moe_route::launch_fuse_shared(topk_weights, topk_ids, num_tokens, top_k,
+                                         shared_expert_ids, routed_scaling_factor,
+                                         static_cast<hipStream_t>(stream));
+}
+
+route_status_t route_sort_ids(float* topk_weights, int32_t* topk_ids, int64_t num_tokens,
+                              int32_t top_k, void* stream) {
+    if (num_tokens < 0 || top_k < 1) return ROUTE_EINVAL;
+    if (top_k > moe_route::kMaxTopK) return ROUTE_ENOTSUP;
+    if (num_tokens == 0) return ROUTE_OK;
+    if (!topk_weights || !topk_ids) return ROUTE_EINVAL;
+    if (!aligned(topk_weights, 4) || !aligned(topk_ids, 4)) return ROUTE_EINVAL;
+    return moe_route::launch_sort_ids(topk_weights, topk_ids, num_tokens, top_k,
+                                      static_cast<hipStream_t>(stream));
+}
+
 const char* route_status_str(route_status_t status) {
     switch (status) {
         case ROUTE_OK: return "ROUTE_OK";

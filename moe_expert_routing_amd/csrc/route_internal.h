@@ -57,5 +57,8 @@ route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
 size_t dispatch_workspace_bytes(int64_t n, int E);
 route_status_t launch_dispatch(const DispatchProblem& d);
+route_status_t launch_fuse_shared(float* w, int32_t* ids, int64_t M, int K,
+                                  const int32_t* shared_ids, float rsf, hipStream_t stream);
+route_status_t launch_sort_ids(float* w, int32_t* ids, int64_t M, int K, hipStream_t stream);
 
 }  // namespace moe_route

@@ -160,3 +160,21 @@ def test_dispatch_binding_has_no_cpu_fallback():
     with pytest.raises(ValueError, match="must live on the GPU"):
         mr.route_dispatch_metadata(torch.zeros(2, 2, dtype=torch.int32), 4,
                                    workspace=torch.zeros(64, dtype=torch.uint8))
+
+
+def test_post_routing_validation():
+    L = mr.lib()
+    f, s = L.route_fuse_shared_expert, L.route_sort_ids
+    assert f(P, Q, -1, 8, R, 2.5, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 4, 1, R, 2.5, None) == mr.ROUTE_EINVAL          # needs two slots
+    assert f(P, Q, 4, 65, R, 2.5, None) == mr.ROUTE_ENOTSUP
+    assert f(P, Q, 4, 8, R, float("nan"), None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 4, 8, R, float("inf"), None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 4, 8, NULL, 2.5, None) == mr.ROUTE_EINVAL
+    assert f(ctypes.c_void_p(0x10002), Q, 4, 8, R, 2.5, None) == mr.ROUTE_EINVAL
+    assert f(NULL, NULL, 0, 8, NULL, 2.5, None) == mr.ROUTE_OK       # empty: no launch
+    assert s(P, Q, -1, 8, None) == mr.ROUTE_EINVAL
+    assert s(P, Q, 4, 0, None) == mr.ROUTE_EINVAL
+    assert s(P, Q, 4, 65, None) == mr.ROUTE_ENOTSUP
+    assert s(P, NULL, 4, 8, None) == mr.ROUTE_EINVAL
+    assert s(NULL, NULL, 0, 8, None) == mr.ROUTE_OK
