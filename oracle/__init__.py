@@ -60,6 +60,8 @@ def _load():
         lib.oracle_fuse_shared_expert.restype = i32
         lib.oracle_sort_ids.argtypes = [p, p, i64, i32]
         lib.oracle_sort_ids.restype = i32
+        lib.oracle_softcap.argtypes = [p, i64, ctypes.c_double]
+        lib.oracle_softcap.restype = i32
         _lib = lib
     return _lib
 
@@ -189,3 +191,12 @@ def sort_ids(topk_weights, topk_ids):
     if rc != 0:
         raise ValueError(f"oracle_sort_ids rejected its arguments (code {rc})")
     return w, ids
+
+
+def softcap(logits, cap):
+    """cap * tanh(logits / cap) in double (cap == 0: unchanged); returns a copy."""
+    x = np.array(logits, dtype=np.float64, copy=True, order="C")
+    rc = _load().oracle_softcap(_ptr(x), x.size, float(cap))
+    if rc != 0:
+        raise ValueError(f"oracle_softcap rejected its arguments (code {rc})")
+    return x

@@ -366,3 +366,16 @@ int oracle_sort_ids(float* weights, int32_t* ids, int64_t M, int K) {
     }
     return 0;
 }
+
+/*
+ * Router logit soft-capping ([ROUTING] section 5): with a non-zero cap the
+ * fused router replaces each logit l by cap * tanh(l / cap) before scoring
+ * (a cap of 0 leaves the logits as they are).  In place, in double.
+ */
+int oracle_softcap(double* logits, int64_t n, double cap) {
+    int64_t i;
+    if (n < 0) return 1;
+    if (cap == 0.0) return 0;
+    for (i = 0; i < n; ++i) logits[i] = cap * tanh(logits[i] / cap);
+    return 0;
+}

@@ -53,3 +53,26 @@ def test_sort_ids_matches_stable_argsort():
     order = np.argsort(i0, axis=1, kind="stable")
     np.testing.assert_array_equal(ids, np.take_along_axis(i0, order, 1))
     np.testing.assert_array_equal(w, np.take_along_axis(w0, order, 1))
+
+
+def test_softcap_closed_forms():
+    cap = 30.0
+    l = np.array([0.0, cap * np.arctanh(0.5), -cap * np.arctanh(0.25), 1e-9, 1e4])
+    y = oracle.softcap(l, cap)
+    np.testing.assert_allclose(y, [0.0, cap / 2, -cap / 4, 1e-9, cap], rtol=1e-14, atol=1e-20)
+    np.testing.assert_array_equal(oracle.softcap(l, 0.0), l)           # cap 0: unchanged
+    x = np.linspace(-5, 5, 101)
+    np.testing.assert_array_equal(oracle.softcap(-x, 7.0), -oracle.softcap(x, 7.0))  # odd
+    assert (np.diff(oracle.softcap(x, 7.0)) > 0).all()                  # strictly increasing
+    assert np.abs(oracle.softcap(x, 1e6) - x).max() < 1e-9               # large cap: identity
+
+
+def test_softcapped_softmax_keeps_topk_ids():
+    """tanh is increasing, so capping changes the softmax weights, never the ids."""
+    rng = np.random.default_rng(2)
+    lg = rng.standard_normal((200, 64)) * 3
+    w0, i0 = oracle.route(lg, 2, scoring=oracle.SOFTMAX, renormalize=False)
+    w1, i1 = oracle.route(oracle.softcap(lg, 5.0), 2, scoring=oracle.SOFTMAX,
+                          renormalize=False)
+    np.testing.assert_array_equal(i0, i1)
+    assert np.abs(w0 - w1).max() > 1e-3
