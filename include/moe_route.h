@@ -142,6 +142,10 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *   hidden_states  [num_tokens, hidden_dim] bf16
  *   router_weight  [hidden_dim, num_experts] bf16 (expert index contiguous)
  *   correction_bias [num_experts] float32 or NULL (zeros)
+ *   logit_softcap  0, or a cap c: every logit l is replaced by c * tanh(l / c)
+ *                  before scoring ([ROUTING] section 5, soft-capping); tanh
+ *                  is increasing, so the cap changes weights, not choices.
+ *                  NaN or infinite caps are ROUTE_EINVAL.
  * Compiled range: num_experts == 256, hidden_dim a positive multiple of 64,
  * hidden_states and router_weight 16-byte aligned; other valid shapes return
  * ROUTE_ENOTSUP.
@@ -151,8 +155,8 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
                                   route_scoring_t scoring_func, const float* correction_bias,
                                   route_group_score_t group_score, int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
-                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
-                                  void* stream);
+                                  int32_t renormalize, float logit_softcap, float* topk_weights,
+                                  int32_t* topk_ids, void* stream);
 
 /*
  * Dispatch metadata of a routing result ([ROUTING] section "output format":

@@ -54,8 +54,8 @@ def lib() -> ctypes.CDLL:
     L.route_topk_softmax.argtypes = [p, i32, i64, i32, i32, i32, p, p, p]
     L.route_grouped_topk.argtypes = [p, i32, i64, i32, i32, i32, i32, i32, i32, p, p, p]
     L.route_biased_grouped_topk.argtypes = [p, i32, p, i64, i32, i32, i32, i32, i32, p, p, p]
-    L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32, p, p,
-                                     p]
+    L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, p, p, p]
     L.route_dispatch_metadata.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p, ctypes.c_size_t,
                                           p]
     L.route_dispatch_workspace_size.argtypes = [i64, i32, i32]
@@ -178,8 +178,10 @@ def route_biased_grouped_topk(gating_output, correction_bias, top_k, num_expert_
 
 def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, topk_group=1,
                        renormalize=False, scoring_func="sigmoid", correction_bias=None,
-                       group_score="top2sum", topk_weights=None, topk_ids=None, stream=None):
-    """bf16 router projection [M,H] x [H,E] fused with routing (logits never stored)."""
+                       group_score="top2sum", topk_weights=None, topk_ids=None, stream=None,
+                       logit_softcap=0.0):
+    """bf16 router projection [M,H] x [H,E] fused with routing (logits never stored);
+    logit_softcap c != 0 replaces each logit l by c * tanh(l / c) before scoring."""
     M, H = hidden_states.shape
     H2, E = router_weight.shape
     if H2 != H:
@@ -197,8 +199,8 @@ def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, 
     _check(lib().route_fused_router(_ptr(hidden_states), _ptr(router_weight), M, H, E,
                                     _scoring_code(scoring_func), _ptr(correction_bias),
                                     rules[group_score], top_k, num_expert_group, topk_group,
-                                    int(bool(renormalize)), _ptr(w), _ptr(ids),
-                                    _stream(hidden_states.device, stream)),
+                                    int(bool(renormalize)), float(logit_softcap), _ptr(w),
+                                    _ptr(ids), _stream(hidden_states.device, stream)),
            "route_fused_router")
     return w, ids
 

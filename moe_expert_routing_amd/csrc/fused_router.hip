@@ -23,7 +23,8 @@
 //   - 16-byte chunks are XOR-swizzled inside LDS rows (by the source address
 //     each lane picks, since a wave's direct-to-LDS write is contiguous) so
 //     that both fragment reads are free of bank conflicts.
-// After the last step the fp32 logits go to LDS and the same routing core as
+// After the last step the fp32 logits (soft-capped when asked) go to LDS and
+// the same routing core as
 // the standalone kernel (route_tile.cuh) routes the 32 rows, 8 lanes per row.
 // The logits never leave the compute unit.
 #include <hip/hip_runtime.h>
@@ -101,7 +102,7 @@ __device__ __forceinline__ int w_swz(int k, int c) { return c ^ (4 * (k & 3)); }
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
-    const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm,
+    const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm, float cap,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
     __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
@@ -239,7 +240,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int m = 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
-            L[m * kFrE + n] = acc[nt][j];
+            // soft-capping (cap != 0): every consumer below sees capped logits
+            L[m * kFrE + n] = cap != 0.0f ? cap * tanh_f32(acc[nt][j] / cap) : acc[nt][j];
         }
     }
     if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
@@ -279,7 +281,7 @@ route_status_t launch_fr(const FusedProblem& f) {
     hipLaunchKernelGGL((fused_router_kernel<SOFTMAX, BIAS, GRP>), dim3((unsigned)blocks),
                        dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
                        static_cast<const uint16_t*>(f.w), p.bias, f.M, f.H, p.TG, p.K,
-                       p.renorm ? 1 : 0, p.weights, p.ids);
+                       p.renorm ? 1 : 0, f.softcap, p.weights, p.ids);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 

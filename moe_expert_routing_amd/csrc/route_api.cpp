@@ -86,17 +86,19 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
                                   route_scoring_t scoring_func, const float* correction_bias,
                                   route_group_score_t group_score, int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
-                                  int32_t renormalize, float* topk_weights, int32_t* topk_ids,
-                                  void* stream) {
+                                  int32_t renormalize, float logit_softcap,
+                                  float* topk_weights, int32_t* topk_ids, void* stream) {
     route_status_t st = check_shape(num_tokens, num_experts, top_k, num_expert_group, topk_group,
                                     group_score);
+    if (!(logit_softcap == logit_softcap) || logit_softcap - logit_softcap != 0.0f)
+        return ROUTE_EINVAL;  // NaN or infinite cap
     if (st != ROUTE_OK) return st;
     if (scoring_func != ROUTE_SOFTMAX && scoring_func != ROUTE_SIGMOID) return ROUTE_EINVAL;
     if (hidden_dim < 1) return ROUTE_EINVAL;
     st = check_io(hidden_states, ROUTE_BF16, correction_bias, num_tokens, topk_weights, topk_ids);
     if (st != ROUTE_OK) return st;
     if (num_tokens > 0 && (!router_weight || !aligned(router_weight, 2))) return ROUTE_EINVAL;
-    FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim,
+    FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim, logit_softcap,
                    RouteProblem{nullptr, ROUTE_BF16, correction_bias, num_tokens, num_experts,
                                 top_k, num_expert_group, topk_group, scoring_func, group_score,
                                 renormalize != 0, topk_weights, topk_ids,

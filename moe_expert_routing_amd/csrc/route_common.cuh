@@ -22,6 +22,13 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
     return fast_rcp(1.0f + fast_exp2(x * -kLog2e));
 }
 
+// tanh(y) = sign(y) * (1 - 2 / (exp(2|y|) + 1)); absolute error ~1e-7, and
+// exactly +-1 once exp overflows.
+__device__ __forceinline__ float tanh_f32(float y) {
+    const float t = fast_exp2(2.0f * kLog2e * fabsf(y));
+    return copysignf(1.0f - 2.0f * fast_rcp(t + 1.0f), y);
+}
+
 // Make the LDS writes of this wave visible to its other lanes before they read.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

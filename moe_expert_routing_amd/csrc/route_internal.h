@@ -28,6 +28,7 @@ struct FusedProblem {
     const void* w;          // [H, E] bf16
     int64_t M;
     int H;
+    float softcap;          // 0: none; else logits -> softcap * tanh(logits / softcap)
     RouteProblem route;     // logits/dtype unused
 };
 

@@ -94,15 +94,15 @@ def test_fused_router_validation():
     L = mr.lib()
     f = L.route_fused_router
     sig, top2 = mr.ROUTE_SIGMOID, mr.ROUTE_GROUP_TOP2_SUM
-    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
     # outside the compiled range
-    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_ENOTSUP
-    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, Q, R, None) == mr.ROUTE_ENOTSUP
-    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, NULL, NULL, None) == \
+    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_ENOTSUP
+    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_ENOTSUP
+    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, 0.0, NULL, NULL, None) == \
         mr.ROUTE_OK
 
 

@@ -57,6 +57,28 @@ def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm):
     _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, renorm, scoring, rule)
 
 
+@pytest.mark.parametrize("M,H,G,TG,K,scoring,rule,bias,renorm,cap", [
+    (200, 256, 1, 1, 2, "softmax", "max", False, False, 30.0),   # top-2 softmax, cap 30
+    (77, 512, 1, 1, 1, "softmax", "max", False, False, 5.0),     # top-1 softmax
+    (96, 128, 8, 4, 8, "sigmoid", "top2sum", True, True, 2.0),   # a cap that saturates
+])
+def test_fused_router_softcap(M, H, G, TG, K, scoring, rule, bias, renorm, cap):
+    """Soft-capped logits: the oracle caps its exact logits in double."""
+    rng = np.random.default_rng(M + H)
+    hidden, w, b = _inputs(rng, M, H, bias=bias)
+    hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32) * np.float32(3))
+    log(f"[gpu] route_fused_router softcap={cap} M={M} H={H} K={K} {scoring}")
+    wt, ids = mr.route_fused_router(to_device(hidden), to_device(w), K, G, TG, renorm, scoring,
+                                    None if b is None else to_device(b), rule,
+                                    logit_softcap=cap)
+    torch.cuda.synchronize()
+    logits = oracle.softcap(oracle.router_logits(hidden, w), cap)
+    rep = compare(logits, wt.cpu().numpy(), ids.cpu().numpy(), scoring=SC[scoring], bias=b, G=G,
+                  TG=TG, rule=RU[rule], K=K, renorm=renorm)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+
+
 @pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
 def test_fused_router_one_lane_holds_most_picks(G, TG):
     """A bias that lifts the first 16 experts puts most of the top 8 of a
