@@ -135,10 +135,9 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
 /*
  * Fused router ([ROUTING] section 5): the router projection
  *   logits[m][e] = sum_h hidden_states[m][h] * router_weight[h][e]
- * with bf16 operands and fp32 accumulation, followed in the same kernel by the
- * routing above (scoring_func, optional correction_bias, group_score rule,
- * num_expert_group / topk_group, top_k, renormalize).  The logits are never
- * written to memory.
+ * with bf16 operands and fp32 accumulation, followed by the routing above
+ * (scoring_func, optional correction_bias, group_score rule,
+ * num_expert_group / topk_group, top_k, renormalize).
  *   hidden_states  [num_tokens, hidden_dim] bf16
  *   router_weight  [hidden_dim, num_experts] bf16 (expert index contiguous)
  *   correction_bias [num_experts] float32 or NULL (zeros)
@@ -146,17 +145,32 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *                  before scoring ([ROUTING] section 5, soft-capping); tanh
  *                  is increasing, so the cap changes weights, not choices.
  *                  NaN or infinite caps are ROUTE_EINVAL.
+ *   workspace      NULL (workspace_bytes 0), or device scratch of at least
+ *                  route_fused_router_workspace_size(num_tokens, hidden_dim,
+ *                  num_experts) bytes, 16-byte aligned, owned by the caller.
+ *                  With NULL, or when that size is 0, one kernel computes
+ *                  the projection and the routing and the logits never reach
+ *                  memory.  Otherwise (fewer than 8192 tokens) the hidden
+ *                  dimension is split over more workgroups: fp32 partial
+ *                  logits and the summed logits go to the workspace, which
+ *                  calls sharing it must not use at the same time.  The two
+ *                  paths add the products in different orders, so their
+ *                  logits may differ in the last bits.
  * Compiled range: num_experts == 256, hidden_dim a positive multiple of 64,
  * hidden_states and router_weight 16-byte aligned; other valid shapes return
- * ROUTE_ENOTSUP.
+ * ROUTE_ENOTSUP.  A misaligned workspace, workspace_bytes without a
+ * workspace, or a workspace smaller than required is ROUTE_EINVAL.
  */
+size_t route_fused_router_workspace_size(int64_t num_tokens, int32_t hidden_dim,
+                                         int32_t num_experts);
 route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
                                   int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
                                   route_scoring_t scoring_func, const float* correction_bias,
                                   route_group_score_t group_score, int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, float logit_softcap, float* topk_weights,
-                                  int32_t* topk_ids, void* stream);
+                                  int32_t* topk_ids, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * Dispatch metadata of a routing result ([ROUTING] section "output format":

@@ -26,6 +26,7 @@ EXPORTED = (
     "route_grouped_topk",
     "route_biased_grouped_topk",
     "route_fused_router",
+    "route_fused_router_workspace_size",
     "route_dispatch_metadata",
     "route_dispatch_workspace_size",
     "route_fuse_shared_expert",
@@ -55,7 +56,9 @@ def lib() -> ctypes.CDLL:
     L.route_grouped_topk.argtypes = [p, i32, i64, i32, i32, i32, i32, i32, i32, p, p, p]
     L.route_biased_grouped_topk.argtypes = [p, i32, p, i64, i32, i32, i32, i32, i32, p, p, p]
     L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32,
-                                     ctypes.c_float, p, p, p]
+                                     ctypes.c_float, p, p, p, ctypes.c_size_t, p]
+    L.route_fused_router_workspace_size.argtypes = [i64, i32, i32]
+    L.route_fused_router_workspace_size.restype = ctypes.c_size_t
     L.route_dispatch_metadata.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p, ctypes.c_size_t,
                                           p]
     L.route_dispatch_workspace_size.argtypes = [i64, i32, i32]
@@ -63,7 +66,7 @@ def lib() -> ctypes.CDLL:
     L.route_sort_ids.argtypes = [p, p, i64, i32, p]
     L.route_dispatch_workspace_size.restype = ctypes.c_size_t
     for name in EXPORTED[:-1]:
-        if name != "route_dispatch_workspace_size":
+        if not name.endswith("_workspace_size"):
             getattr(L, name).restype = i32
     L.route_status_str.argtypes = [i32]
     L.route_status_str.restype = ctypes.c_char_p
@@ -176,12 +179,23 @@ def route_biased_grouped_topk(gating_output, correction_bias, top_k, num_expert_
     return w, ids
 
 
+def route_fused_router_workspace_size(num_tokens, hidden_dim, num_experts) -> int:
+    """Bytes of device workspace the few-token path of route_fused_router uses
+    (0: that shape runs as one kernel)."""
+    return int(lib().route_fused_router_workspace_size(num_tokens, hidden_dim, num_experts))
+
+
 def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, topk_group=1,
                        renormalize=False, scoring_func="sigmoid", correction_bias=None,
                        group_score="top2sum", topk_weights=None, topk_ids=None, stream=None,
-                       logit_softcap=0.0):
-    """bf16 router projection [M,H] x [H,E] fused with routing (logits never stored);
-    logit_softcap c != 0 replaces each logit l by c * tanh(l / c) before scoring."""
+                       logit_softcap=0.0, workspace=None):
+    """bf16 router projection [M,H] x [H,E] followed by routing; logit_softcap
+    c != 0 replaces each logit l by c * tanh(l / c) before scoring.
+
+    workspace: None allocates the workspace the library asks for (a uint8
+    device tensor from torch's caching allocator), False passes none (always
+    the single fused kernel), or a uint8 device tensor of at least
+    route_fused_router_workspace_size(M, H, E) bytes."""
     M, H = hidden_states.shape
     H2, E = router_weight.shape
     if H2 != H:
@@ -195,12 +209,21 @@ def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, 
         if correction_bias.dtype != torch.float32 or tuple(correction_bias.shape) != (E,):
             raise ValueError("correction_bias must be float32 of shape [E]")
     w, ids = _outputs(M, top_k, hidden_states.device, topk_weights, topk_ids)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is None:
+        need = route_fused_router_workspace_size(M, H, E)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=hidden_states.device)
+    if workspace is not None and workspace is not False:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+        _need_device(workspace)
     _need_device(hidden_states, router_weight, correction_bias, w, ids)
     _check(lib().route_fused_router(_ptr(hidden_states), _ptr(router_weight), M, H, E,
                                     _scoring_code(scoring_func), _ptr(correction_bias),
                                     rules[group_score], top_k, num_expert_group, topk_group,
                                     int(bool(renormalize)), float(logit_softcap), _ptr(w),
-                                    _ptr(ids), _stream(hidden_states.device, stream)),
+                                    _ptr(ids), ws_ptr, ws_bytes,
+                                    _stream(hidden_states.device, stream)),
            "route_fused_router")
     return w, ids
 

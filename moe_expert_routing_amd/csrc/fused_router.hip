@@ -29,6 +29,8 @@
 // The logits never leave the compute unit.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "route_common.cuh"
 #include "route_internal.h"
 #include "route_tile.cuh"
@@ -99,19 +101,21 @@ __device__ __forceinline__ void barrier_no_fence() {
 __device__ __forceinline__ int a_swz(int m, int c) { return c ^ ((m >> 1) & 7); }
 __device__ __forceinline__ int w_swz(int k, int c) { return c ^ (4 * (k & 3)); }
 
-template <bool SOFTMAX, bool BIAS, int GRP>
-__global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
-    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
-    const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm, float cap,
-    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
-    __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
-    __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
-    __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
-
+// The projection of one workgroup: acc = hidden rows m0 .. m0+31 (rows past M
+// read row M-1) times W over the hidden steps s_lo .. s_lo+steps-1 (kFrBK
+// hidden units each), in the MFMA layout the epilogues below unpack.  The
+// copy wave (its return value true) leaves acc alone.  Returns after every
+// copy has landed and a workgroup barrier, so the caller may reuse sA and sW.
+__device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
+                                           const uint16_t* __restrict__ w, int64_t M, int H,
+                                           int64_t m0, int s_lo, int steps,
+                                           unsigned char (*sA)[kFrABytes],
+                                           unsigned char (*sW)[kFrWBytes], f32x16 (&acc)[2]) {
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
-    const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
+    hidden += (int64_t)s_lo * kFrBK;
+    w += (int64_t)s_lo * kFrBK * kFrE;
 
     // Direct-to-LDS copy assignment: every copy writes a 1 KiB block, lane l
     // its chunk l, and reads the global chunk that the swizzle puts there.
@@ -153,7 +157,6 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     // 16kk + 8(g/2) + 4h + (l%16)/4 and experts n0 + 16(g%2) + 4(l%4) .. +3.
     const int fa_m = lane % 32;
     const int g = lane / 16, gi = lane % 16;
-    f32x16 acc[2];
 #pragma unroll
     for (int q = 0; q < 16; ++q) { acc[0][q] = 0.f; acc[1][q] = 0.f; }
 
@@ -203,7 +206,6 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     // copies of step s reuse.  Copies past the last step repeat it into a stage
     // that is never read again, so the count in flight is the same at every
     // step.  Both kinds of wave pass the same number of barriers.
-    const int steps = H / kFrBK;
     if (copier) {
         for (int q = 0; q < kFrAAhead; ++q) issue_a(min(q, steps - 1), q);
         int ia = 0;
@@ -230,6 +232,24 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    return copier;
+}
+
+template <bool SOFTMAX, bool BIAS, int GRP>
+__global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm, float cap,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
+    __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
+    __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
+    __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
+
+    const int t = threadIdx.x;
+    const int lane = t % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
+    f32x16 acc[2];
+    const bool copier = fr_project(hidden, w, M, H, m0, 0, H / kFrBK, sA, sW, acc);
 
     // ---- epilogue: logits to LDS, then route the 32 rows (8 lanes per row)
     float* L = reinterpret_cast<float*>(sW[0]);  // [32][256] fp32 logits
@@ -274,6 +294,115 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
         id_out, [&](int e) { return lrow[e]; });
 }
 
+// ---- few tokens: the hidden dimension split over workgroups
+//
+// With fewer than 256 row tiles the single kernel leaves compute units idle
+// and each workgroup walks all of H one W tile after the other.  The split
+// path gives workgroup (tile, s) the hidden steps of split s only; it writes
+// its fp32 partial logits to part[s][M][256].  A second kernel sums the
+// splits of each logit in a fixed order (so results do not depend on timing)
+// and soft-caps the sum, and the standalone routing kernel routes the fp32
+// logits.
+__global__ __launch_bounds__(kFrThreads) void fused_router_partial_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w, int64_t M, int H,
+    int nsplit, float* __restrict__ part) {
+    __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
+    __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
+
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
+    const int split = blockIdx.y, steps_all = H / kFrBK;
+    const int s_lo = split * steps_all / nsplit, s_hi = (split + 1) * steps_all / nsplit;
+    f32x16 acc[2];
+    if (fr_project(hidden, w, M, H, m0, s_lo, s_hi - s_lo, sA, sW, acc)) return;
+
+    float* out = part + (int64_t)split * M * kFrE;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int n = wv * 64 + nt * 32 + (lane % 32);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t row = m0 + 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
+            if (row < M) out[row * kFrE + n] = acc[nt][j];
+        }
+    }
+}
+
+// logits[m][e] = sum of part[s][m][e] over the splits, then the soft cap.
+// A block holds 1024 threads: 64 float4 columns x S split slices x 16/S
+// rows.  Slice q sums splits q, q+S, q+2S, ... in that order; slice sums are
+// then added in slice order.
+template <int S>
+__global__ __launch_bounds__(1024) void fr_reduce_kernel(const float* __restrict__ part,
+                                                         int64_t M, int nsplit, float cap,
+                                                         float* __restrict__ logits) {
+    constexpr int R = 16 / S;
+    __shared__ float4 red[S][R][64];
+    const int c4 = threadIdx.x % 64, q = (threadIdx.x / 64) % S, r = threadIdx.x / (64 * S);
+    const int64_t row = (int64_t)blockIdx.x * R + r;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < M) {
+        const float4* src = reinterpret_cast<const float4*>(part) + row * 64 + c4;
+        const int64_t split_stride = M * 64;
+#pragma unroll 4
+        for (int sp = q; sp < nsplit; sp += S) {
+            const float4 v = src[sp * split_stride];
+            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+    }
+    red[q][r][c4] = a;
+    __syncthreads();
+    if (q != 0 || row >= M) return;
+#pragma unroll
+    for (int j = 1; j < S; ++j) {
+        const float4 v = red[j][r][c4];
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    if (cap != 0.0f) {
+        a.x = cap * tanh_f32(a.x / cap);
+        a.y = cap * tanh_f32(a.y / cap);
+        a.z = cap * tanh_f32(a.z / cap);
+        a.w = cap * tanh_f32(a.w / cap);
+    }
+    reinterpret_cast<float4*>(logits)[row * 64 + c4] = a;
+}
+
+route_status_t launch_split(const FusedProblem& f, int nsplit) {
+    const RouteProblem& p = f.route;
+    const int64_t tiles = (f.M + kFrRows - 1) / kFrRows;
+    float* part = f.workspace;
+    float* logits = part + (int64_t)nsplit * f.M * kFrE;
+    hipLaunchKernelGGL(fused_router_partial_kernel, dim3((unsigned)tiles, (unsigned)nsplit),
+                       dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                       static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
+    if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
+    const int S = nsplit >= 16 ? 16 : nsplit >= 8 ? 8 : nsplit >= 4 ? 4 : 2;
+    const dim3 rgrid((unsigned)((f.M + 16 / S - 1) / (16 / S)));
+    switch (S) {
+        case 16:
+            hipLaunchKernelGGL(fr_reduce_kernel<16>, rgrid, dim3(1024), 0, p.stream, part, f.M,
+                               nsplit, f.softcap, logits);
+            break;
+        case 8:
+            hipLaunchKernelGGL(fr_reduce_kernel<8>, rgrid, dim3(1024), 0, p.stream, part, f.M,
+                               nsplit, f.softcap, logits);
+            break;
+        case 4:
+            hipLaunchKernelGGL(fr_reduce_kernel<4>, rgrid, dim3(1024), 0, p.stream, part, f.M,
+                               nsplit, f.softcap, logits);
+            break;
+        default:
+            hipLaunchKernelGGL(fr_reduce_kernel<2>, rgrid, dim3(1024), 0, p.stream, part, f.M,
+                               nsplit, f.softcap, logits);
+    }
+    if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
+    RouteProblem rp = p;
+    rp.logits = logits;
+    rp.dtype = ROUTE_F32;
+    return launch_route(rp);
+}
+
 template <bool SOFTMAX, bool BIAS, int GRP>
 route_status_t launch_fr(const FusedProblem& f) {
     const RouteProblem& p = f.route;
@@ -299,8 +428,31 @@ bool fused_router_supported(const FusedProblem& f) {
     return !(p.scoring == ROUTE_SOFTMAX && p.rule == ROUTE_GROUP_TOP2_SUM);
 }
 
+int fused_router_splits(int64_t M, int H) {
+    // One workgroup fills a compute unit (its LDS), so up to 256 workgroups
+    // run in one round.  Split as far as one round allows, then back off to
+    // the fewest splits that keep the same steps per workgroup (every split
+    // costs partial-logit traffic).  From 129 row tiles on no split fits.
+    const int64_t tiles = (M + kFrRows - 1) / kFrRows;
+    const int steps = H / kFrBK;
+    if (M <= 0 || steps < 2) return 1;
+    const int64_t most = std::min<int64_t>(steps, 256 / tiles);
+    if (most < 2) return 1;
+    const int per_split = (steps + (int)most - 1) / (int)most;
+    return (steps + per_split - 1) / per_split;
+}
+
+size_t fused_router_workspace_bytes(int64_t M, int H) {
+    const int n = fused_router_splits(M, H);
+    return n == 1 ? 0 : sizeof(float) * kFrE * (size_t)M * (size_t)(n + 1);
+}
+
 route_status_t launch_fused_router(const FusedProblem& f) {
     const RouteProblem& p = f.route;
+    if (f.workspace != nullptr) {
+        const int nsplit = fused_router_splits(f.M, f.H);
+        if (nsplit > 1) return launch_split(f, nsplit);
+    }
     const bool soft = p.scoring == ROUTE_SOFTMAX;
     const bool bias = p.bias != nullptr;
     if (p.G == 1) {

@@ -81,13 +81,21 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
     return route_common(p);
 }
 
+size_t route_fused_router_workspace_size(int64_t num_tokens, int32_t hidden_dim,
+                                         int32_t num_experts) {
+    if (num_tokens <= 0 || hidden_dim < 1 || num_experts != 256 || hidden_dim % 64 != 0)
+        return 0;
+    return moe_route::fused_router_workspace_bytes(num_tokens, hidden_dim);
+}
+
 route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
                                   int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
                                   route_scoring_t scoring_func, const float* correction_bias,
                                   route_group_score_t group_score, int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, float logit_softcap,
-                                  float* topk_weights, int32_t* topk_ids, void* stream) {
+                                  float* topk_weights, int32_t* topk_ids, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
     route_status_t st = check_shape(num_tokens, num_experts, top_k, num_expert_group, topk_group,
                                     group_score);
     if (!(logit_softcap == logit_softcap) || logit_softcap - logit_softcap != 0.0f)
@@ -98,12 +106,19 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
     st = check_io(hidden_states, ROUTE_BF16, correction_bias, num_tokens, topk_weights, topk_ids);
     if (st != ROUTE_OK) return st;
     if (num_tokens > 0 && (!router_weight || !aligned(router_weight, 2))) return ROUTE_EINVAL;
-    FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim, logit_softcap,
+    if (workspace == nullptr ? workspace_bytes != 0 : !aligned(workspace, 16))
+        return ROUTE_EINVAL;
+    FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim, logit_softcap, nullptr,
                    RouteProblem{nullptr, ROUTE_BF16, correction_bias, num_tokens, num_experts,
                                 top_k, num_expert_group, topk_group, scoring_func, group_score,
                                 renormalize != 0, topk_weights, topk_ids,
                                 static_cast<hipStream_t>(stream)}};
     if (!moe_route::fused_router_supported(f)) return ROUTE_ENOTSUP;
+    if (workspace != nullptr) {
+        if (workspace_bytes < moe_route::fused_router_workspace_bytes(num_tokens, hidden_dim))
+            return ROUTE_EINVAL;
+        f.workspace = static_cast<float*>(workspace);
+    }
     if (num_tokens == 0) return ROUTE_OK;
     return moe_route::launch_fused_router(f);
 }

@@ -90,7 +90,6 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     int renorm, float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     constexpr int E = LPR * VPL;
     constexpr int RPW = kWave / LPR;               // rows per wave
-    constexpr int CPL = VPL / 4;                   // 16-byte chunks per lane
     static_assert(GRP == 0 || VPL % SPLIT == 0, "a group splits evenly");
     static_assert(E <= 512, "9 index bits");
     static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");

@@ -29,6 +29,7 @@ struct FusedProblem {
     int64_t M;
     int H;
     float softcap;          // 0: none; else logits -> softcap * tanh(logits / softcap)
+    float* workspace;       // fused_router_workspace_bytes(M, H), or nullptr: one kernel
     RouteProblem route;     // logits/dtype unused
 };
 
@@ -56,6 +57,8 @@ constexpr int kMaxGroups = 64;
 route_status_t launch_route(const RouteProblem& p);
 route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
+int fused_router_splits(int64_t M, int H);  // hidden-dimension splits (1: one kernel)
+size_t fused_router_workspace_bytes(int64_t M, int H);
 size_t dispatch_workspace_bytes(int64_t n, int E);
 route_status_t launch_dispatch(const DispatchProblem& d);
 route_status_t launch_fuse_shared(float* w, int32_t* ids, int64_t M, int K,

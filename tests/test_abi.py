@@ -94,16 +94,51 @@ def test_fused_router_validation():
     L = mr.lib()
     f = L.route_fused_router
     sig, top2 = mr.ROUTE_SIGMOID, mr.ROUTE_GROUP_TOP2_SUM
-    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
     # outside the compiled range
-    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_ENOTSUP
-    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, None) == mr.ROUTE_ENOTSUP
-    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, 0.0, NULL, NULL, None) == \
+    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
+    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
+    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, 0.0, NULL, NULL, NULL, 0, None) == \
         mr.ROUTE_OK
+    # NaN or infinite caps
+    for cap in (float("nan"), float("inf"), -float("inf")):
+        assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, cap, Q, R, NULL, 0, None) == \
+            mr.ROUTE_EINVAL
+    # workspace: a size without a pointer, a misaligned one, one too small
+    need = L.route_fused_router_workspace_size(8, 7168, 256)
+    assert need > 0
+    W = ctypes.c_void_p(0x40000)
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, need, None) == \
+        mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, ctypes.c_void_p(0x40008),
+             need, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, W, need - 4, None) == \
+        mr.ROUTE_EINVAL
+
+
+def test_fused_router_workspace_size():
+    ws = mr.lib().route_fused_router_workspace_size
+    assert ws(0, 7168, 256) == 0
+    assert ws(-1, 7168, 256) == 0
+    assert ws(8, 7168, 128) == 0          # outside the compiled range
+    assert ws(8, 7000, 256) == 0
+    assert ws(1, 64, 256) == 0            # one hidden step: nothing to split
+    assert ws(8192, 7168, 256) == 0       # 256 row tiles of 32: one kernel
+    assert ws(4097, 7168, 256) == 0       # 129 tiles: 2 splits would need 2 rounds
+    assert ws(2720, 7168, 256) == 4 * 256 * 2720 * 4   # 85 tiles: 3 splits of 38 steps
+    assert ws(65536, 7168, 256) == 0
+    # fp32 partials of every split plus the summed logits, [M][256] each.
+    # One row tile and 112 steps of 64: 112 splits of one step.
+    assert ws(1, 7168, 256) == 4 * 256 * 1 * 113
+    assert ws(32, 7168, 256) == 4 * 256 * 32 * 113
+    # 3 tiles: 56 splits of two steps (168 workgroups, one round)
+    assert ws(65, 7168, 256) == 4 * 256 * 65 * 57
+    # 128 tiles: 2 splits of 56 steps (256 workgroups)
+    assert ws(4096, 7168, 256) == 4 * 256 * 4096 * 3
 
 
 def test_binding_has_no_cpu_fallback():

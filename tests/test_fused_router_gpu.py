@@ -24,9 +24,10 @@ def _inputs(rng, M, H, E=256, bias=True):
     return hidden, w, b
 
 
-def _run(hidden, w, b, K, G, TG, renorm, scoring, rule):
+def _run(hidden, w, b, K, G, TG, renorm, scoring, rule, workspace=None, cap=0.0):
     wt, ids = mr.route_fused_router(to_device(hidden), to_device(w), K, G, TG, renorm, scoring,
-                                    None if b is None else to_device(b), rule)
+                                    None if b is None else to_device(b), rule,
+                                    logit_softcap=cap, workspace=workspace)
     torch.cuda.synchronize()
     return wt.cpu().numpy(), ids.cpu().numpy()
 
@@ -48,12 +49,17 @@ def _check(hidden, w, b, wt, ids, rows, K, G, TG, renorm, scoring, rule):
     (96, 192, 8, 2, 4, "sigmoid", "max", False, True),        # sigmoid, no bias
     (1, 64, 8, 4, 8, "sigmoid", "top2sum", True, True),       # single token
 ])
-def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm):
+@pytest.mark.parametrize("path", ["one_kernel", "default"])
+def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm, path):
+    """path one_kernel passes no workspace (projection and routing in one
+    kernel); default lets the binding pass the workspace the library asks for
+    (the split path whenever H spans two or more steps of 64)."""
     rng = np.random.default_rng(M * 1000 + H)
     hidden, w, b = _inputs(rng, M, H, bias=bias)
     log(f"[gpu] route_fused_router M={M} H={H} G={G} TG={TG} K={K} {scoring} {rule} "
-        f"bias={bias}")
-    wt, ids = _run(hidden, w, b, K, G, TG, renorm, scoring, rule)
+        f"bias={bias} {path}")
+    wt, ids = _run(hidden, w, b, K, G, TG, renorm, scoring, rule,
+                   workspace=False if path == "one_kernel" else None)
     _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, renorm, scoring, rule)
 
 
@@ -89,9 +95,73 @@ def test_fused_router_one_lane_holds_most_picks(G, TG):
     hidden, w, b = _inputs(rng, M, H)
     b[:16] += np.float32(0.6)
     log(f"[gpu] route_fused_router skewed bias G={G} TG={TG}")
-    wt, ids = _run(hidden, w, b, 8, G, TG, True, "sigmoid", "top2sum")
+    wt, ids = _run(hidden, w, b, 8, G, TG, True, "sigmoid", "top2sum", workspace=False)
     assert (ids < 16).sum(axis=1).mean() > 6  # most rows take 5+ picks from one lane
     _check(hidden, w, b, wt, ids, np.arange(M), 8, G, TG, True, "sigmoid", "top2sum")
+
+
+@pytest.mark.parametrize("M,H,G,TG,K,scoring,rule,bias,renorm,cap", [
+    (1, 7168, 8, 4, 8, "sigmoid", "top2sum", True, True, 0.0),      # 112 one-step splits
+    (7, 448, 8, 4, 8, "sigmoid", "top2sum", True, False, 0.0),      # 7 splits
+    (77, 1024, 1, 1, 8, "sigmoid", "top2sum", True, True, 0.0),     # 3 tiles, ungrouped
+    (300, 640, 8, 3, 6, "softmax", "max", False, False, 0.0),       # 10 tiles, softmax
+    (1000, 384, 1, 1, 2, "softmax", "max", False, False, 30.0),     # top-2 softmax, capped
+    (130, 7168, 8, 4, 8, "sigmoid", "top2sum", True, True, 2.0),    # saturating cap
+])
+def test_fused_router_split_path(M, H, G, TG, K, scoring, rule, bias, renorm, cap):
+    """Few tokens: the hidden dimension is split over workgroups, partial
+    logits summed by a second kernel and routed by the routing kernel."""
+    assert mr.route_fused_router_workspace_size(M, H, 256) > 0
+    rng = np.random.default_rng(M * 7 + H)
+    hidden, w, b = _inputs(rng, M, H, bias=bias)
+    if cap:
+        hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32) * np.float32(3))
+    log(f"[gpu] route_fused_router split path M={M} H={H} G={G} TG={TG} K={K} {scoring} "
+        f"cap={cap}")
+    wt, ids = _run(hidden, w, b, K, G, TG, renorm, scoring, rule, cap=cap)
+    logits = oracle.router_logits(hidden, w)
+    if cap:
+        logits = oracle.softcap(logits, cap)
+    rep = compare(logits, wt, ids, scoring=SC[scoring], bias=b, G=G, TG=TG, rule=RU[rule], K=K,
+                  renorm=renorm)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+    # the single fused kernel on the same input agrees with the oracle as well
+    wt1, ids1 = _run(hidden, w, b, K, G, TG, renorm, scoring, rule, workspace=False, cap=cap)
+    rep1 = compare(logits, wt1, ids1, scoring=SC[scoring], bias=b, G=G, TG=TG, rule=RU[rule],
+                   K=K, renorm=renorm)
+    assert rep1.ok(), rep1.summary()
+
+
+def test_fused_router_split_path_full_width_sampled():
+    """128 row tiles of the 7168-wide router: two splits of 56 steps."""
+    wl = WORKLOADS["fused_router_h7168"]
+    M = 4096
+    assert mr.route_fused_router_workspace_size(M, wl.hidden_dim, wl.E) == 4 * 256 * M * 3
+    hidden, w = make_router_inputs(wl, M)
+    b = make_bias(wl)
+    log(f"[gpu] route_fused_router split path M={M} H={wl.hidden_dim} (2 splits)")
+    wt, ids = _run(hidden, w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(M - 40, M),
+                                     np.arange(31, M, 512), np.arange(32, M, 512),
+                                     rng.choice(M, 64, replace=False)]))
+    _check(hidden, w, b, wt, ids, rows, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
+
+
+def test_fused_router_split_path_deterministic_and_reused_workspace():
+    """Two calls through one caller-owned workspace, the second smaller:
+    bit-identical to fresh calls (the sums run in a fixed order)."""
+    rng = np.random.default_rng(13)
+    hidden, w, b = _inputs(rng, 200, 1024)
+    ws = torch.empty(mr.route_fused_router_workspace_size(200, 1024, 256), dtype=torch.uint8,
+                     device="cuda")
+    a = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    c = _run(hidden[:50], w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    a2 = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    c2 = _run(hidden[:50], w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    assert np.array_equal(a[0], a2[0]) and np.array_equal(a[1], a2[1])
+    assert np.array_equal(c[0], c2[0]) and np.array_equal(c[1], c2[1])
 
 
 def test_fused_router_full_workload_sampled():
