@@ -418,6 +418,7 @@ route_status_t launch_fr(const FusedProblem& f) {
 
 bool fused_router_supported(const FusedProblem& f) {
     const RouteProblem& p = f.route;
+    if (p.E != kFrE) return small_router_supported(f);
     const uintptr_t a = reinterpret_cast<uintptr_t>(f.hidden) | reinterpret_cast<uintptr_t>(f.w) |
                         reinterpret_cast<uintptr_t>(p.bias);
     if (p.E != kFrE || f.H % kFrBK != 0 || (a % 16) != 0 || p.K > 8) return false;
@@ -449,6 +450,7 @@ size_t fused_router_workspace_bytes(int64_t M, int H) {
 
 route_status_t launch_fused_router(const FusedProblem& f) {
     const RouteProblem& p = f.route;
+    if (p.E != kFrE) return launch_small_router(f);
     if (f.workspace != nullptr) {
         const int nsplit = fused_router_splits(f.M, f.H);
         if (nsplit > 1) return launch_split(f, nsplit);

@@ -1,0 +1,282 @@
+// Fused router for few experts (E = 8 or 16) on the vector ALUs (gfx950).
+//
+// "[SGLang] MoE routing: token-to-expert assignment algorithms", section 5:
+// besides the tensor-core router, the page has a plain elementwise router
+// (each logit a product summed along the hidden dimension) followed by
+// optional soft-capping and a softmax top-1/top-2, and sends small batches
+// and routers with at most 8 experts to it.  With 8 or 16 experts a matrix
+// instruction would leave most of its tile empty, and the projection reads
+// 2H bytes of hidden state per token against 2E·H multiply-adds, so on
+// MI355X this path is bound by reading the hidden states at every batch
+// size; it serves all M for these expert counts.
+//
+// Layout.  A block of 4 waves routes groups of T = 8 tokens (persistent
+// blocks stride over the groups); the waves take turns over chunks of the
+// hidden dimension.  Each lane owns a slice of 8 experts (E / 8 slices over
+// the wave) and 8 consecutive hidden units: one 16-byte load per token and
+// the lane's 16-byte slice of the 8 matching W rows.  Pairs of hidden units
+// meet v_dot2_f32_bf16 (two bf16 products added to an fp32 accumulator);
+// v_perm_b32 pairs the two W rows' entries of one expert to match.  Each lane
+// keeps T x 8 fp32 partial sums, and W is read once per 8 tokens; the next
+// chunk's loads are issued before the current chunk's products.  The block
+// then sums the partials of its lanes in LDS in a fixed order, soft-caps the
+// logits and one lane per token routes (softmax or sigmoid, optional bias,
+// top-K by (score desc, index asc), optional renormalisation).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "route_common.cuh"
+#include "route_internal.h"
+
+namespace moe_route {
+namespace {
+
+constexpr int kSrWaves = 4;
+constexpr int kSrThreads = kSrWaves * kWave;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// One token's routing over its E logits (cap already applied): scores,
+// selection scores c = s + bias, K picks by (c desc, index asc), weights s
+// of the picks, optionally divided by their sum (added in pick order).
+template <int E, bool SOFTMAX, bool BIAS>
+__device__ __forceinline__ void route_token(const float (&x)[E], const float* __restrict__ bias,
+                                            int K, int renorm, float* __restrict__ w_row,
+                                            int32_t* __restrict__ id_row) {
+    float s[E], c[E];
+    if constexpr (SOFTMAX) {
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) mx = fmaxf(mx, x[e]);
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            s[e] = fast_exp2((x[e] - mx) * kLog2e);
+            sum += s[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = s[e] / sum;
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] = sigmoid_f32(x[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) c[e] = BIAS ? s[e] + bias[e] : s[e];
+
+    int slot[E];  // pick rank of each expert, -1 if not picked
+#pragma unroll
+    for (int e = 0; e < E; ++e) slot[e] = -1;
+    float tot = 0.f;
+    for (int k = 0; k < K; ++k) {
+        float bv = -INFINITY, bs = 0.f;
+        int bi = E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            // scanning e upwards with a strict > keeps the lower index on ties
+            if (slot[e] < 0 && (c[e] > bv || bi == E)) { bv = c[e]; bi = e; bs = s[e]; }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) slot[e] = e == bi ? k : slot[e];
+        tot += bs;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (slot[e] >= 0) {
+            w_row[slot[e]] = renorm ? s[e] / tot : s[e];
+            id_row[slot[e]] = e;
+        }
+    }
+}
+
+constexpr int kSrTokens = 8;  // tokens per group
+
+template <int E, bool SOFTMAX, bool BIAS>
+__global__ __launch_bounds__(kSrThreads) void small_router_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int64_t M, int H, int K, int renorm, float cap,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
+    constexpr int T = kSrTokens;
+    constexpr int NS = E / 8;          // expert slices per wave
+    constexpr int LPS = kWave / NS;    // lanes per slice
+    constexpr int UPC = 8 * LPS;       // hidden units per wave and chunk
+    constexpr int NV = T * 8;          // partial sums per lane
+    static_assert(NV % 32 == 0, "partials are reduced 32 at a time");
+    __shared__ __align__(16) float red[32][kSrThreads + 4];
+    __shared__ float logit[T * E];
+
+    const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+    const int es = lane / LPS, lp = lane % LPS;
+    const int64_t groups = (M + T - 1) / T;
+    const int chunks = (H + UPC - 1) / UPC;
+
+    struct Chunk {
+        uint4 hv[T];
+        uint4 wr[8];
+    };
+    float acc[T][8];
+#pragma unroll
+    for (int tk = 0; tk < T; ++tk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[tk][e] = 0.f;
+
+    // Loads of chunk c (c < chunks) of group g.  Lanes past H load unit 0
+    // and zero it; rows past M read row M-1 (never stored).
+    auto load = [&](int64_t g, int c, Chunk& b) __attribute__((always_inline)) {
+        const int h = c * UPC + 8 * lp;
+        const int hc = h < H ? h : 0;
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk)
+            b.hv[tk] = *reinterpret_cast<const uint4*>(hidden + min(g * T + tk, M - 1) * H + hc);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            b.wr[r] = *reinterpret_cast<const uint4*>(w + (int64_t)(hc + r) * E + 8 * es);
+        if (c * UPC + UPC > H && h >= H) {
+#pragma unroll
+            for (int tk = 0; tk < T; ++tk) b.hv[tk] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto compute = [&](const Chunk& b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {  // hidden units 8 lp + 2p, 8 lp + 2p + 1
+            const uint32_t* lo = reinterpret_cast<const uint32_t*>(&b.wr[2 * p]);
+            const uint32_t* hi = reinterpret_cast<const uint32_t*>(&b.wr[2 * p + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // slice experts 2j, 2j + 1
+                const uint32_t we = __builtin_amdgcn_perm(hi[j], lo[j], 0x05040100u);
+                const uint32_t wo = __builtin_amdgcn_perm(hi[j], lo[j], 0x07060302u);
+#pragma unroll
+                for (int tk = 0; tk < T; ++tk) {
+                    const uint32_t a = reinterpret_cast<const uint32_t*>(&b.hv[tk])[p];
+                    acc[tk][2 * j] = dot2(a, we, acc[tk][2 * j]);
+                    acc[tk][2 * j + 1] = dot2(a, wo, acc[tk][2 * j + 1]);
+                }
+            }
+        }
+    };
+
+    // Sum the block's partials of group g, soft-cap them and route its
+    // tokens; acc is cleared for the next group.
+    auto finish = [&](int64_t g) __attribute__((always_inline)) {
+        const int64_t m0 = g * T;
+        // Sum the partials, 32 values per round.  Thread t writes its values
+        // to column t.  Columns come in blocks of 32 lanes (one slice of a
+        // wave, or half a slice when E = 8); the threads of output
+        // (value j, slice s) add one such block each, blocks in a fixed
+        // order, then combine by butterfly.  The order never changes, so
+        // results do not depend on timing.
+#pragma unroll
+        for (int r = 0; r < NV / 32; ++r) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) red[j][t] = acc[(32 * r + j) / 8][(32 * r + j) % 8];
+            __syncthreads();
+            constexpr int TPO = kSrThreads / 32 / NS;  // threads per output
+            const int o = t / TPO, q = t % TPO;
+            const int j = o % 32, s = o / 32;
+            const int cb = q * NS + s;   // column block: lanes 32 (cb % 2) .. of wave cb / 2
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 d = *reinterpret_cast<const float4*>(&red[j][32 * cb + 4 * i]);
+                v += (d.x + d.y) + (d.z + d.w);
+            }
+#pragma unroll
+            for (int x = TPO / 2; x > 0; x >>= 1) v += shfl_xor(v, x);
+            if (q == 0) {
+                const int vi = 32 * r + j;  // token vi / 8, expert 8 s + vi % 8
+                logit[(vi / 8) * E + 8 * s + vi % 8] = cap != 0.0f ? cap * tanh_f32(v / cap) : v;
+            }
+            __syncthreads();
+        }
+
+        if (t < T && m0 + t < M) {
+            float x[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = logit[t * E + e];
+            route_token<E, SOFTMAX, BIAS>(x, bias, K, renorm, w_out + (m0 + t) * K,
+                                          id_out + (m0 + t) * K);
+        }
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[tk][e] = 0.f;
+    };
+
+    // Each wave streams its (group, chunk) items -- chunks wv, wv + 4, ...
+    // of groups blockIdx.x, blockIdx.x + gridDim.x, ... -- through two
+    // buffers: the loads of the next item, possibly of the next group, are in
+    // flight while the current one is computed and while a finished group is
+    // reduced.  Every wave finishes each group once, so all pass the same
+    // barriers.  The last item's successor repeats it (one load, no branch).
+    const int n = wv < chunks ? (chunks - 1 - wv) / kSrWaves + 1 : 0;  // items per group
+    int64_t g = blockIdx.x;
+    if (n == 0) {
+        for (; g < groups; g += gridDim.x) finish(g);
+        return;
+    }
+    int k = 0;  // item of group g held in the current buffer
+    auto step = [&](Chunk& cur, Chunk& nxt) __attribute__((always_inline)) {
+        int64_t g2 = g;
+        int k2 = k + 1;
+        if (k2 == n) { g2 = g + gridDim.x; k2 = 0; }
+        const bool more = g2 < groups;
+        load(more ? g2 : g, wv + kSrWaves * (more ? k2 : k), nxt);
+        compute(cur);
+        if (k + 1 == n) finish(g);
+        g = g2;
+        k = k2;
+        return g < groups;
+    };
+    Chunk A, B;
+    load(g, wv, A);
+    while (step(A, B) && step(B, A)) {
+    }
+}
+
+template <int E, bool SOFTMAX, bool BIAS>
+route_status_t launch_sr(const FusedProblem& f) {
+    const RouteProblem& p = f.route;
+    auto kernel = small_router_kernel<E, SOFTMAX, BIAS>;
+    static int resident = 0;  // blocks per CU for this instantiation
+    if (resident == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kSrThreads, 0) !=
+                hipSuccess || n <= 0)
+            n = 1;
+        resident = n;
+    }
+    const int64_t groups = (f.M + kSrTokens - 1) / kSrTokens;
+    const int64_t blocks = std::min<int64_t>(groups, (int64_t)device_cu_count() * resident);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSrThreads), 0, p.stream,
+                       static_cast<const uint16_t*>(f.hidden), static_cast<const uint16_t*>(f.w),
+                       p.bias, f.M, f.H, p.K, p.renorm ? 1 : 0, f.softcap, p.weights, p.ids);
+    return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
+}
+
+template <int E>
+route_status_t launch_sr_e(const FusedProblem& f) {
+    const RouteProblem& p = f.route;
+    if (p.scoring == ROUTE_SOFTMAX) return launch_sr<E, true, false>(f);
+    return p.bias ? launch_sr<E, false, true>(f) : launch_sr<E, false, false>(f);
+}
+
+}  // namespace
+
+bool small_router_supported(const FusedProblem& f) {
+    const RouteProblem& p = f.route;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(f.hidden) | reinterpret_cast<uintptr_t>(f.w);
+    if ((p.E != 8 && p.E != 16) || f.H % 8 != 0 || (a % 16) != 0) return false;
+    if (p.G != 1) return false;
+    return !(p.scoring == ROUTE_SOFTMAX && p.bias != nullptr);
+}
+
+route_status_t launch_small_router(const FusedProblem& f) {
+    return f.route.E == 8 ? launch_sr_e<8>(f) : launch_sr_e<16>(f);
+}
+
+}  // namespace moe_route

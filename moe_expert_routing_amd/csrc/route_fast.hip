@@ -157,19 +157,6 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     }
 }
 
-int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 template <typename T, int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP, int SPLIT, int TL,
           int KMAX>
@@ -236,6 +223,20 @@ route_status_t dispatch_lpr8(const RouteProblem& p, bool& handled) {
 }
 
 }  // namespace
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 route_status_t launch_route(const RouteProblem& p) {
     const size_t esz = p.dtype == ROUTE_F32 ? 4 : 2;

@@ -52,11 +52,15 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 64;
 
+int device_cu_count();  // compute units of the current device (cached)
+
 // Kernel launchers (route_kernels.hip / fused_router.hip).  They assume a
 // validated problem with M > 0 and return ROUTE_OK or ROUTE_ELAUNCH.
 route_status_t launch_route(const RouteProblem& p);
 route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
+bool small_router_supported(const FusedProblem& p);  // E = 8 or 16 (fused_router_small.hip)
+route_status_t launch_small_router(const FusedProblem& p);
 int fused_router_splits(int64_t M, int H);  // hidden-dimension splits (1: one kernel)
 size_t fused_router_workspace_bytes(int64_t M, int H);
 size_t dispatch_workspace_bytes(int64_t n, int E);

@@ -120,6 +120,29 @@ def test_fused_router_validation():
         mr.ROUTE_EINVAL
 
 
+def test_fused_router_few_experts_range():
+    """8 or 16 experts go to the vector-ALU router: H a multiple of 8, no
+    expert groups; other expert counts below 256 are outside the range."""
+    f = mr.lib().route_fused_router
+    sm, top2, mx = mr.ROUTE_SOFTMAX, mr.ROUTE_GROUP_TOP2_SUM, mr.ROUTE_GROUP_MAX
+    ok = mr.ROUTE_OK
+    assert f(NULL, NULL, 0, 4096, 8, sm, NULL, mx, 2, 1, 1, 0, 30.0, NULL, NULL, NULL, 0,
+             None) == ok
+    assert f(NULL, NULL, 0, 4096, 16, sm, NULL, mx, 2, 1, 1, 0, 0.0, NULL, NULL, NULL, 0,
+             None) == ok
+    assert f(P, Q, 8, 4100, 8, sm, NULL, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_ENOTSUP                                  # H % 8 != 0
+    assert f(P, Q, 8, 4096, 12, sm, NULL, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_ENOTSUP                                  # 12 experts
+    assert f(P, Q, 8, 4096, 8, sm, NULL, top2, 2, 2, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_ENOTSUP                                  # expert groups
+    assert f(P, Q, 8, 4096, 8, sm, R, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_ENOTSUP                                  # softmax with a bias
+    assert f(P, Q, 8, 4096, 8, sm, NULL, mx, 9, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_EINVAL                                   # K > E
+    assert mr.lib().route_fused_router_workspace_size(64, 4096, 8) == 0
+
+
 def test_fused_router_workspace_size():
     ws = mr.lib().route_fused_router_workspace_size
     assert ws(0, 7168, 256) == 0

@@ -1,0 +1,93 @@
+"""GPU parity of route_fused_router with 8 or 16 experts (the vector-ALU
+router: bf16 dot products on v_dot2_f32_bf16, optional soft-cap, then a
+per-token top-k) against the oracle's exact double logits."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_routing_amd as mr
+import oracle
+from gpu_util import log, to_device
+from parity_check import compare
+from workloads import WORKLOADS, bf16_bits_from_f32, make_router_inputs
+
+pytestmark = pytest.mark.gpu
+
+SC = {"sigmoid": oracle.SIGMOID, "softmax": oracle.SOFTMAX}
+
+
+def _inputs(rng, M, H, E, scale=1.0, bias=False):
+    hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32) *
+                                np.float32(scale))
+    w = bf16_bits_from_f32(rng.standard_normal((H, E), dtype=np.float32) * np.float32(H ** -0.5))
+    b = (rng.standard_normal(E, dtype=np.float32) * np.float32(0.1)) if bias else None
+    return hidden, w, b
+
+
+def _run_check(hidden, w, b, E, K, scoring, renorm, cap, rows=None):
+    wt, ids = mr.route_fused_router(to_device(hidden), to_device(w), K, 1, 1, renorm, scoring,
+                                    None if b is None else to_device(b), "max",
+                                    logit_softcap=cap)
+    torch.cuda.synchronize()
+    wt, ids = wt.cpu().numpy(), ids.cpu().numpy()
+    rows = np.arange(hidden.shape[0]) if rows is None else rows
+    logits = oracle.router_logits(hidden[rows], w)
+    if cap:
+        logits = oracle.softcap(logits, cap)
+    rep = compare(logits, wt[rows], ids[rows], scoring=SC[scoring], bias=b, G=1, TG=1,
+                  rule=oracle.GROUP_MAX, K=K, renorm=renorm)
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+    return wt, ids
+
+
+@pytest.mark.parametrize("M,H,E,K,scoring,bias,renorm,cap,scale", [
+    (1, 4096, 8, 2, "softmax", False, False, 0.0, 1.0),     # one token
+    (37, 4096, 8, 2, "softmax", False, True, 30.0, 1.0),    # ragged block of 8 tokens
+    (100, 4104, 8, 1, "softmax", False, False, 5.0, 3.0),   # H past a 512 chunk; top-1
+    (64, 8, 8, 2, "softmax", False, False, 0.0, 1.0),       # H = 8: one lane's units
+    (300, 2048, 8, 8, "sigmoid", True, True, 0.0, 1.0),     # sigmoid + bias, K = E
+    (50, 6144, 16, 4, "softmax", False, True, 0.0, 1.0),    # 16 experts
+    (19, 1000, 16, 2, "sigmoid", False, False, 2.0, 3.0),   # 16 experts, saturating cap
+    (256, 512, 16, 16, "softmax", False, False, 0.0, 1.0),  # K = E = 16
+])
+def test_small_router(M, H, E, K, scoring, bias, renorm, cap, scale):
+    rng = np.random.default_rng(M * 31 + H + E)
+    hidden, w, b = _inputs(rng, M, H, E, scale, bias)
+    log(f"[gpu] route_fused_router E={E} M={M} H={H} K={K} {scoring} bias={bias} cap={cap}")
+    _run_check(hidden, w, b, E, K, scoring, renorm, cap)
+
+
+def test_small_router_workload_sampled():
+    wl = WORKLOADS["fused_router_e8_h4096"]
+    hidden, w = make_router_inputs(wl)
+    log(f"[gpu] route_fused_router workload={wl.name} M={wl.M} H={wl.hidden_dim}")
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([np.arange(24), np.arange(wl.M - 24, wl.M),
+                                     rng.choice(wl.M, 200, replace=False)]))
+    wt, ids = _run_check(hidden, w, None, wl.E, wl.K, wl.scoring, wl.renormalize, wl.softcap,
+                         rows)
+    # every row: distinct ids in range, softmax weights in (0, 1], descending
+    assert np.all((ids >= 0) & (ids < wl.E)) and np.all(ids[:, 0] != ids[:, 1])
+    assert np.all((wt > 0) & (wt <= 1)) and np.all(wt[:, 0] >= wt[:, 1])
+
+
+def test_small_router_deterministic():
+    rng = np.random.default_rng(17)
+    hidden, w, _ = _inputs(rng, 77, 3072, 8)
+    x, wr = to_device(hidden), to_device(w)
+    a = mr.route_fused_router(x, wr, 2, 1, 1, False, "softmax", None, "max")
+    c = mr.route_fused_router(x, wr, 2, 1, 1, False, "softmax", None, "max")
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_small_router_rejects_outside_range():
+    x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    for E in (8, 12):                               # H % 8 != 0; 12 experts
+        wr = torch.zeros((100, E), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(ValueError, match="compiled range"):
+            mr.route_fused_router(x, wr, 2, 1, 1)
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="compiled range"):
+        mr.route_fused_router(x, wr, 2, 2, 1)      # expert groups

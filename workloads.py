@@ -54,6 +54,7 @@ class Workload:
     bias: str | None = None  # None, "uniform:<a>" (U(-a, a)) or "normal:<std>"
     hidden_dim: int = 0    # fused router only
     w_std: float = 0.0     # fused router only
+    softcap: float = 0.0   # fused router only: logits -> c * tanh(logits / c)
 
 
 WORKLOADS = {
@@ -80,6 +81,12 @@ WORKLOADS = {
                                    group_rule="top2sum", renormalize=True, dtype="bf16",
                                    bias="normal:" + repr(0.02 ** 0.5), hidden_dim=7168,
                                    w_std=(1.0 / 7168) ** 0.5),
+    # Fused router with few experts (Mixtral/Grok-like: hidden 4096, 8
+    # experts, top-2 softmax, logits soft-capped at 30), the vector-ALU path.
+    "fused_router_e8_h4096": Workload("fused_router_e8_h4096", "route_fused_router",
+                                      M=8192, E=8, K=2, scoring="softmax", renormalize=False,
+                                      dtype="bf16", hidden_dim=4096, w_std=(1.0 / 4096) ** 0.5,
+                                      softcap=30.0),
 }
 
 BIASED_GROUPED_M_SWEEP = (1, 4, 16, 64, 128, 1024, 8192, 65536)
