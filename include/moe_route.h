@@ -156,10 +156,14 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *                  calls sharing it must not use at the same time.  The two
  *                  paths add the products in different orders, so their
  *                  logits may differ in the last bits.
- * Compiled range: num_experts == 256, hidden_dim a positive multiple of 64,
- * hidden_states and router_weight 16-byte aligned; other valid shapes return
- * ROUTE_ENOTSUP.  A misaligned workspace, workspace_bytes without a
- * workspace, or a workspace smaller than required is ROUTE_EINVAL.
+ * Compiled range, with hidden_states and router_weight 16-byte aligned:
+ *   num_experts == 256: hidden_dim a positive multiple of 64 (MFMA router);
+ *   num_experts 8 or 16 ([ROUTING] section 5's small-router case):
+ *     hidden_dim a positive multiple of 8, num_expert_group == 1; no
+ *     workspace is used (its size is 0).
+ * Other valid shapes return ROUTE_ENOTSUP.  A misaligned workspace,
+ * workspace_bytes without a workspace, or a workspace smaller than required
+ * is ROUTE_EINVAL.
  */
 size_t route_fused_router_workspace_size(int64_t num_tokens, int32_t hidden_dim,
                                          int32_t num_experts);

@@ -1,27 +1,32 @@
-// Fused router for few experts (E = 8 or 16) on the vector ALUs (gfx950).
+// Fused router for few experts (E = 8 or 16), gfx950.
 //
 // "[SGLang] MoE routing: token-to-expert assignment algorithms", section 5:
 // besides the tensor-core router, the page has a plain elementwise router
 // (each logit a product summed along the hidden dimension) followed by
 // optional soft-capping and a softmax top-1/top-2, and sends small batches
-// and routers with at most 8 experts to it.  With 8 or 16 experts a matrix
-// instruction would leave most of its tile empty, and the projection reads
-// 2H bytes of hidden state per token against 2E·H multiply-adds, so on
-// MI355X this path is bound by reading the hidden states at every batch
-// size; it serves all M for these expert counts.
+// and routers with at most 8 experts to it.  Here two kernels serve these
+// expert counts at every batch size; both read the hidden states once, which
+// bounds them (2H bytes per token against 2EH multiply-adds):
 //
-// Layout.  A block of 4 waves routes groups of T = 8 tokens (persistent
-// blocks stride over the groups); the waves take turns over chunks of the
-// hidden dimension.  Each lane owns a slice of 8 experts (E / 8 slices over
-// the wave) and 8 consecutive hidden units: one 16-byte load per token and
-// the lane's 16-byte slice of the 8 matching W rows.  Pairs of hidden units
-// meet v_dot2_f32_bf16 (two bf16 products added to an fp32 accumulator);
-// v_perm_b32 pairs the two W rows' entries of one expert to match.  Each lane
-// keeps T x 8 fp32 partial sums, and W is read once per 8 tokens; the next
-// chunk's loads are issued before the current chunk's products.  The block
-// then sums the partials of its lanes in LDS in a fixed order, soft-caps the
-// logits and one lane per token routes (softmax or sigmoid, optional bias,
-// top-K by (score desc, index asc), optional renormalisation).
+//  - an MFMA kernel (hidden_dim <= 8192): 16-token tiles on
+//    v_mfma_f32_16x16x32_bf16, W held in registers (described below);
+//  - a vector-ALU kernel: bf16 pairs on v_dot2_f32_bf16, used for more than
+//    8192 hidden units, and for 8 experts below 4096 tokens, where its
+//    8-token blocks spread over more compute units than 16-token tiles do.
+//
+// Vector-ALU layout.  A block of 4 waves routes groups of T = 8 tokens
+// (persistent blocks stride over the groups); the waves take turns over
+// chunks of the hidden dimension.  Each lane owns a slice of 8 experts
+// (E / 8 slices over the wave) and 8 consecutive hidden units: one 16-byte
+// load per token and the lane's 16-byte slice of the 8 matching W rows.
+// Pairs of hidden units meet v_dot2_f32_bf16 (two bf16 products added to an
+// fp32 accumulator); v_perm_b32 pairs the two W rows' entries of one expert
+// to match.  Each lane keeps T x 8 fp32 partial sums, and W is read once per
+// 8 tokens; the next chunk's loads are issued before the current chunk's
+// products.  The block then sums the partials of its lanes in LDS in a fixed
+// order, soft-caps the logits and one lane per token routes (softmax or
+// sigmoid, optional bias, top-K by (score desc, index asc), optional
+// renormalisation).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -258,9 +263,245 @@ route_status_t launch_sr(const FusedProblem& f) {
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 
+// One token's routing over 16 consecutive lanes: lane j holds expert j's
+// logit x (cap applied); lanes j >= E hold none.  Same rule as route_token:
+// K rounds of a butterfly argmax by (c desc, index asc), weights s of the
+// picks added in pick order; the pick of rank k is stored by its lane.
+template <int E, bool SOFTMAX, bool BIAS>
+__device__ __forceinline__ void route_lanes16(float x, int j, bool store,
+                                              const float* __restrict__ bias, int K, int renorm,
+                                              float* __restrict__ w_row,
+                                              int32_t* __restrict__ id_row) {
+    const bool live = j < E;
+    float s;
+    if constexpr (SOFTMAX) {
+        float mx = live ? x : -INFINITY;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+        const float u = live ? fast_exp2((x - mx) * kLog2e) : 0.f;
+        float sum = u;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) sum += shfl_xor(sum, o);
+        s = u / sum;
+    } else {
+        s = sigmoid_f32(x);
+    }
+    const float c = BIAS && live ? s + bias[j] : s;
+    bool open = live;  // not picked yet
+    int rank = -1;
+    float tot = 0.f;
+    for (int k = 0; k < K; ++k) {
+        float bv = open ? c : -INFINITY, bs = s;
+        int bi = open ? j : 0x7fffffff;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+            const float ov = shfl_xor(bv, o), os = shfl_xor(bs, o);
+            const int oi = shfl_xor(bi, o);
+            if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; bs = os; }
+        }
+        if (bi == j) { rank = k; open = false; }
+        tot += bs;
+    }
+    if (store && rank >= 0) {
+        w_row[rank] = renorm ? s / tot : s;
+        id_row[rank] = j;
+    }
+}
+
+// ---- MFMA variant (hidden_dim <= 8192)
+//
+// The projection is a [M, H] x [H, E] product with E <= 16, which fits
+// v_mfma_f32_16x16x32_bf16 (16 tokens x 32 hidden units x 16 experts; with
+// E = 8 half of the tile's columns are zero).  A block of 8 waves fills a
+// compute unit (256 registers per lane) and strides over tiles of 16 tokens.
+// The 32-unit fragments of H are dealt to the waves round-robin (fragment f
+// to wave f mod 8), and each wave keeps its fragments of W in registers as MFMA B operands for the
+// whole launch.  A operands come straight from global memory: in the MFMA
+// layout, lane (token i, quarter q) of fragment f holds hidden units
+// 32 f + 8 q .. +7 of token i, one 16-byte load.  A wave loads its
+// fragments 4 at a time into two register buffers, the next batch (or the
+// next tile's first) in flight while the current one is multiplied and while
+// a finished tile is reduced.  Partial tiles of the 8 waves are added in LDS
+// in wave order, then soft-capped and routed by 16 lanes per token.
+constexpr int kSmWaves = 8;
+constexpr int kSmThreads = kSmWaves * kWave;
+constexpr int kSmTile = 16;      // tokens per tile
+constexpr int kSmFragMax = 32;   // fragments per wave: hidden_dim <= 8 * 32 * 32
+constexpr int kSmBatch = 4;      // fragments per load batch
+constexpr int kSmHMax = kSmWaves * kSmFragMax * 32;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int E, int NB, bool SOFTMAX, bool BIAS>
+__global__ __launch_bounds__(kSmThreads) void small_router_mfma_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
+    const float* __restrict__ bias, int64_t M, int H, int K, int renorm, float cap,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
+    __shared__ float part[kSmWaves][kSmTile * 16];
+    __shared__ __align__(16) unsigned char wstage[kSmWaves][kSmBatch * 1024];
+
+    const int t = threadIdx.x, lane = t % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int i16 = lane % 16, q = lane / 16;
+    const int nf = (H + 31) / 32;
+    const int fw = wv < nf ? (nf - 1 - wv) / kSmWaves + 1 : 0;  // fragments of this wave
+    // Every wave runs NB batches of 4 fragments (NB = ceil(ceil(nf / 8) / 4));
+    // fragments a wave does not have are loaded from a clamped address,
+    // zeroed and multiplied as zeros, so no load sits under a branch.
+    const int64_t tiles = (M + kSmTile - 1) / kSmTile;
+
+    // B operands: lane (expert i16, quarter q) of fragment i holds
+    // W[32 f + 8 q + j][i16], j = 0..7, f = wv + 8 i; zeros past H or E.
+    // Each fragment's 32 W rows are one contiguous piece of W: the wave loads
+    // it with 16-byte loads into an LDS image of 32 rows x 16 experts (E = 8
+    // rows padded with zeros), four fragments at a time, and the transposing
+    // read ds_read_b64_tr_b16 turns the image into B operands: in a 16-lane
+    // group, lane j receives element j % 4 of the 8-byte rows addressed by
+    // lanes j / 4 + 4 m, m = 0..3, so lane a points at row 8 q + 4 h + a / 4,
+    // experts 4 (a % 4) .. +3, and lane j gets k = 8 q + 4 h + m of expert j.
+    constexpr int FM = NB * kSmBatch;  // fragment slots per wave
+    static_assert(FM <= kSmFragMax, "fragments per wave");
+    bf16x8 wf[FM];
+    {
+        uint4 raw[FM];
+        const int row = lane / 2, half = lane % 2;  // this lane's 16 bytes of an image
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int k = 32 * (wv + kSmWaves * i) + row;
+            const bool ok = i < fw && k < H && (E == 16 || half == 0);
+            raw[i] = *reinterpret_cast<const uint4*>(w + (ok ? (int64_t)k * E + 8 * half : 0));
+            if (!ok) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        unsigned char* img = wstage[wv];
+#pragma unroll
+        for (int rr = 0; rr < NB; ++rr) {
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i)
+                *reinterpret_cast<uint4*>(img + 1024 * i + 16 * lane) = raw[kSmBatch * rr + i];
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i) {
+                i16x4 h2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int off = 1024 * i + 32 * (8 * q + 4 * h + i16 / 4) + 8 * (i16 % 4);
+                    h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(img + off));
+                }
+                wf[kSmBatch * rr + i] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            wave_lds_sync();
+        }
+    }
+
+    struct Batch {
+        uint4 a[kSmBatch];
+    };
+    // Batch b of tile g: fragments 4b .. 4b+3 of this wave.  Rows past M read
+    // row M-1 (never stored); units past H are zero.
+    auto load = [&](int64_t g, int b, Batch& x) __attribute__((always_inline)) {
+        const int64_t row = min(g * kSmTile + i16, M - 1);
+        const uint16_t* hr = hidden + row * H;
+#pragma unroll
+        for (int i = 0; i < kSmBatch; ++i) {
+            const int fi = kSmBatch * b + i;
+            const int k = 32 * (wv + kSmWaves * fi) + 8 * q;
+            const bool ok = fi < fw && k < H;
+            x.a[i] = *reinterpret_cast<const uint4*>(hr + (ok ? k : 0));
+            if (!ok) x.a[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    f32x4 c0, c1;
+    auto compute = [&](const Batch& x, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kSmBatch; ++i) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, x.a[i]);
+            if (i % 2 == 0)
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[kSmBatch * b + i], c0, 0, 0, 0);
+            else
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[kSmBatch * b + i], c1, 0, 0, 0);
+        }
+    };
+
+    // Two batch buffers: batch b + 1 loads while batch b is multiplied, and
+    // the next tile's first batch is in flight while this tile is reduced.
+    Batch P[2];
+    int64_t g = blockIdx.x;
+    load(g, 0, P[0]);
+    for (; g < tiles; g += gridDim.x) {
+        const int64_t gn = g + gridDim.x < tiles ? g + gridDim.x : g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { c0[r] = 0.f; c1[r] = 0.f; }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b + 1 < NB) load(g, b + 1, P[(b + 1) % 2]);
+            compute(P[b % 2], b);
+        }
+        load(gn, 0, P[0]);
+
+        // D layout: lane (expert i16, quarter q) holds tokens 4q .. 4q+3
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wv][(4 * q + r) * 16 + i16] = c0[r] + c1[r];
+        __syncthreads();
+        // thread t < 256: token t / 16, expert t % 16 (the 16 lanes of a token
+        // are consecutive); partials added in wave order
+        float v = 0.f;
+        if (t < kSmTile * 16) {
+#pragma unroll
+            for (int x = 0; x < kSmWaves; ++x) v += part[x][t];
+            if (cap != 0.0f) v = cap * tanh_f32(v / cap);
+        }
+        __syncthreads();  // part is free for the next tile
+        const int64_t row = g * kSmTile + t / 16;
+        if (t < kSmTile * 16)
+            route_lanes16<E, SOFTMAX, BIAS>(v, t % 16, row < M, bias, K, renorm, w_out + row * K,
+                                            id_out + row * K);
+    }
+}
+
+template <int E, int NB, bool SOFTMAX, bool BIAS>
+route_status_t launch_sm_nb(const FusedProblem& f) {
+    const RouteProblem& p = f.route;
+    const int64_t tiles = (f.M + kSmTile - 1) / kSmTile;
+    const int64_t blocks = std::min<int64_t>(tiles, (int64_t)device_cu_count());
+    hipLaunchKernelGGL((small_router_mfma_kernel<E, NB, SOFTMAX, BIAS>), dim3((unsigned)blocks),
+                       dim3(kSmThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                       static_cast<const uint16_t*>(f.w), p.bias, f.M, f.H, p.K,
+                       p.renorm ? 1 : 0, f.softcap, p.weights, p.ids);
+    return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
+}
+
+template <int E, bool SOFTMAX, bool BIAS>
+route_status_t launch_sm(const FusedProblem& f) {
+    const int nf = (f.H + 31) / 32;
+    const int nb = ((nf + kSmWaves - 1) / kSmWaves + kSmBatch - 1) / kSmBatch;
+    switch (nb) {
+        case 1: return launch_sm_nb<E, 1, SOFTMAX, BIAS>(f);
+        case 2: return launch_sm_nb<E, 2, SOFTMAX, BIAS>(f);
+        case 3: return launch_sm_nb<E, 3, SOFTMAX, BIAS>(f);
+        case 4: return launch_sm_nb<E, 4, SOFTMAX, BIAS>(f);
+        case 5: return launch_sm_nb<E, 5, SOFTMAX, BIAS>(f);
+        case 6: return launch_sm_nb<E, 6, SOFTMAX, BIAS>(f);
+        case 7: return launch_sm_nb<E, 7, SOFTMAX, BIAS>(f);
+        default: return launch_sm_nb<E, 8, SOFTMAX, BIAS>(f);
+    }
+}
+
 template <int E>
 route_status_t launch_sr_e(const FusedProblem& f) {
     const RouteProblem& p = f.route;
+    // One MFMA block per 16-token tile leaves compute units idle below 256
+    // tiles; with 8 experts the vector-ALU kernel (8 tokens per block, half
+    // the work per token of 16 experts) measured faster there.
+    const bool mfma = f.H <= kSmHMax && (E == 16 || f.M >= 256 * kSmTile);
+    if (mfma) {
+        if (p.scoring == ROUTE_SOFTMAX) return launch_sm<E, true, false>(f);
+        return p.bias ? launch_sm<E, false, true>(f) : launch_sm<E, false, false>(f);
+    }
     if (p.scoring == ROUTE_SOFTMAX) return launch_sr<E, true, false>(f);
     return p.bias ? launch_sr<E, false, true>(f) : launch_sr<E, false, false>(f);
 }

@@ -1,6 +1,6 @@
-"""GPU parity of route_fused_router with 8 or 16 experts (the vector-ALU
-router: bf16 dot products on v_dot2_f32_bf16, optional soft-cap, then a
-per-token top-k) against the oracle's exact double logits."""
+"""GPU parity of route_fused_router with 8 or 16 experts against the
+oracle's exact double logits: the MFMA kernel (hidden_dim <= 8192) and the
+vector-ALU kernel (larger hidden_dim), optional soft-cap, per-token top-k."""
 import numpy as np
 import pytest
 import torch
@@ -50,6 +50,10 @@ def _run_check(hidden, w, b, E, K, scoring, renorm, cap, rows=None):
     (50, 6144, 16, 4, "softmax", False, True, 0.0, 1.0),    # 16 experts
     (19, 1000, 16, 2, "sigmoid", False, False, 2.0, 3.0),   # 16 experts, saturating cap
     (256, 512, 16, 16, "softmax", False, False, 0.0, 1.0),  # K = E = 16
+    (4000, 7168, 16, 2, "softmax", False, True, 0.0, 1.0),  # 250 tiles, 28 fragments a wave
+    (4100, 1000, 8, 2, "softmax", False, False, 5.0, 3.0),  # 8 experts on MFMA, ragged H
+    (33, 9000, 8, 2, "softmax", False, False, 30.0, 1.0),   # H > 8192: vector-ALU kernel
+    (20, 8704, 16, 3, "sigmoid", True, True, 0.0, 1.0),     # H > 8192, 16 experts
 ])
 def test_small_router(M, H, E, K, scoring, bias, renorm, cap, scale):
     rng = np.random.default_rng(M * 31 + H + E)
