@@ -135,7 +135,9 @@ def time_calls(launch, n_sets, stream, steps=400, warmup=40):
 
 
 def measure_all(out_path=None):
-    """Every workload (each config, the biased-grouped M sweep, the fused router)."""
+    """Every workload: each config, the biased-grouped M sweep, the fused
+    routers (7168-wide at 8192 and few tokens, 8 experts), dispatch metadata
+    and the post-routing steps."""
     import numpy as np
     import torch
 
@@ -215,6 +217,86 @@ def measure_all(out_path=None):
          "frac_mfma_bf16_kernel": flops / (kern * 1e-6) / 2.5e15}
     results.append(r)
     eprint(json.dumps(r))
+    def graph_us(fn, n=20, reps=5):
+        """Per-call time (us) of fn from a replayed HIP graph of n calls:
+        kernel time plus the gaps between kernels, without host launch cost."""
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(n):
+                    fn(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = _events(2)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / n)
+        return float(np.median(ts))
+
+    # few tokens through the 7168-wide router: split path (workspace) and
+    # the single fused kernel, graph replay
+    for Ms in (1, 64, 1024, 4096):
+        xs_ = hd[:Ms].contiguous()
+        o_ = (torch.empty(Ms, wl.K, device=dev), torch.empty(Ms, wl.K, dtype=torch.int32,
+                                                            device=dev))
+        need = mr.route_fused_router_workspace_size(Ms, H, E)
+        wsp = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def fr_call(st, ws_arg):
+            mr.route_fused_router(xs_, wd, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", bd,
+                                  "top2sum", o_[0], o_[1], stream=st, workspace=ws_arg)
+        t_split = graph_us(lambda st: fr_call(st, wsp))
+        t_one = graph_us(lambda st: fr_call(st, False))
+        r = {"workload": "fused_router_h7168_few_tokens", "entry": wl.entry, "M": Ms, "H": H,
+             "E": E, "K": wl.K, "splits": need // (4 * E * Ms) - 1 if need else 1,
+             "us_per_call_graph_split": t_split, "us_per_call_graph_one_kernel": t_one}
+        results.append(r)
+        eprint(json.dumps(r))
+
+    # few experts: 8-expert router, hidden 4096, top-2 softmax, cap 30
+    wl8 = WORKLOADS["fused_router_e8_h4096"]
+    h8, w8 = make_router_inputs(wl8)
+    h8d, w8d = dev_tensor(h8), dev_tensor(w8)
+    for Ms in (1, 64, 2048, wl8.M):
+        xs_ = h8d[:Ms].contiguous()
+        o_ = (torch.empty(Ms, wl8.K, device=dev), torch.empty(Ms, wl8.K, dtype=torch.int32,
+                                                             device=dev))
+
+        def sr_call(st):
+            mr.route_fused_router(xs_, w8d, wl8.K, 1, 1, wl8.renormalize, wl8.scoring, None,
+                                  "max", o_[0], o_[1], stream=st, logit_softcap=wl8.softcap)
+        t = graph_us(sr_call)
+        nbytes = Ms * wl8.hidden_dim * 2 + wl8.hidden_dim * wl8.E * 2 + Ms * wl8.K * 8
+        r = {"workload": wl8.name, "entry": wl8.entry, "M": Ms, "H": wl8.hidden_dim,
+             "E": wl8.E, "K": wl8.K, "softcap": wl8.softcap, "us_per_call_graph": t,
+             "alg_bytes": nbytes, "GBps": nbytes / (t * 1e-6) / 1e9,
+             "note": "warm (graph replay of one input set)"}
+        if Ms == wl8.M:
+            sets8 = [xs_] + [xs_.clone() for _ in range(4)]
+            outs8 = [(torch.empty(Ms, wl8.K, device=dev),
+                      torch.empty(Ms, wl8.K, dtype=torch.int32, device=dev)) for _ in range(5)]
+
+            def launch8(i):
+                mr.route_fused_router(sets8[i], w8d, wl8.K, 1, 1, wl8.renormalize, wl8.scoring,
+                                      None, "max", outs8[i][0], outs8[i][1], stream=stream,
+                                      logit_softcap=wl8.softcap)
+            per_call, kern = time_calls(launch8, 5, stream, steps=200, warmup=20)
+            r.update({"rotating_sets": 5, "us_per_call_cold": per_call,
+                      "GBps_cold": nbytes / (per_call * 1e-6) / 1e9,
+                      "frac_hbm_cold": nbytes / (per_call * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+        results.append(r)
+        eprint(json.dumps(r))
+
     # dispatch metadata of the 65536-token biased grouped routing output
     wl = WORKLOADS["biased_grouped_e256"]
     xb = dev_tensor(make_logits(wl))
@@ -236,6 +318,31 @@ def measure_all(out_path=None):
          "kernel_us": kern, "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
          "note": "three kernels per call; us_per_call includes the library's allocations "
                  "of the outputs in the Python binding"}
+    results.append(r)
+    eprint(json.dumps(r))
+    # post-routing steps on the 65536 x 8 routing output (in place)
+    n_sets = 16
+    shared = torch.randint(0, wl.E, (wl.M,), dtype=torch.int32, device=dev)
+    w_sets = [rw.clone() for _ in range(n_sets)]
+    id_sets = [rids.clone() for _ in range(n_sets)]
+
+    def launch_shared(i):
+        mr.route_fuse_shared_expert(w_sets[i], id_sets[i], shared, 2.5, stream=stream)
+    per_call, kern = time_calls(launch_shared, n_sets, stream, steps=400, warmup=20)
+    nbytes = wl.M * wl.K * 8 + wl.M * 4 + wl.M * 8  # read w, ids; shared ids; write last slot
+    r = {"workload": "fuse_shared_expert_m65536_k8", "entry": "route_fuse_shared_expert",
+         "M": wl.M, "K": wl.K, "rotating_sets": n_sets, "us_per_call": per_call,
+         "kernel_us": kern, "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9}
+    results.append(r)
+    eprint(json.dumps(r))
+
+    def launch_sort(i):
+        mr.route_sort_ids(w_sets[i], id_sets[i], stream=stream)
+    per_call, kern = time_calls(launch_sort, n_sets, stream, steps=400, warmup=20)
+    nbytes = 2 * wl.M * wl.K * 8  # read and write weights and ids
+    r = {"workload": "sort_ids_m65536_k8", "entry": "route_sort_ids", "M": wl.M, "K": wl.K,
+         "rotating_sets": n_sets, "us_per_call": per_call, "kernel_us": kern,
+         "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9}
     results.append(r)
     eprint(json.dumps(r))
     if out_path:
