@@ -276,9 +276,18 @@ def measure_all(out_path=None):
             mr.route_fused_router(xs_, w8d, wl8.K, 1, 1, wl8.renormalize, wl8.scoring, None,
                                   "max", o_[0], o_[1], stream=st, logit_softcap=wl8.softcap)
         t = graph_us(sr_call)
+        # context: the unfused pair, torch's bf16 matmul (hipBLASLt) then the
+        # routing kernel, without the cap
+        lg = torch.empty(Ms, wl8.E, dtype=torch.bfloat16, device=dev)
+
+        def unfused(st):
+            torch.matmul(xs_, w8d, out=lg)
+            mr.route_topk_softmax(lg, wl8.K, wl8.renormalize, o_[0], o_[1], stream=st)
+        t_unfused = graph_us(unfused)
         nbytes = Ms * wl8.hidden_dim * 2 + wl8.hidden_dim * wl8.E * 2 + Ms * wl8.K * 8
         r = {"workload": wl8.name, "entry": wl8.entry, "M": Ms, "H": wl8.hidden_dim,
              "E": wl8.E, "K": wl8.K, "softcap": wl8.softcap, "us_per_call_graph": t,
+             "us_per_call_graph_torch_matmul_then_routing": t_unfused,
              "alg_bytes": nbytes, "GBps": nbytes / (t * 1e-6) / 1e9,
              "note": "warm (graph replay of one input set)"}
         if Ms == wl8.M:
