@@ -202,14 +202,23 @@ def measure_all(out_path=None):
     outs = [(torch.empty(M, wl.K, device=dev), torch.empty(M, wl.K, dtype=torch.int32,
                                                            device=dev)) for _ in range(n_sets)]
 
-    def launch_fr(i):
+    ws_fr = torch.empty(max(mr.route_fused_router_workspace_size(M, H, E), 16),
+                        dtype=torch.uint8, device=dev)
+
+    def launch_fr(i, ws_arg=ws_fr):
         mr.route_fused_router(hs[i], wd, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", bd,
-                              "top2sum", outs[i][0], outs[i][1], stream=stream)
+                              "top2sum", outs[i][0], outs[i][1], stream=stream,
+                              workspace=ws_arg)
+    # the library's default for this shape (two hidden splits of 64-row tiles
+    # with partial logits in the workspace), then the single fused kernel
     per_call, kern = time_calls(launch_fr, n_sets, stream, steps=200, warmup=20)
+    per_call_one, kern_one = time_calls(lambda i: launch_fr(i, False), n_sets, stream,
+                                        steps=200, warmup=20)
     nbytes = M * H * 2 + H * E * 2 + E * 4 + M * wl.K * 8
     flops = 2.0 * M * H * E
     r = {"workload": wl.name, "entry": wl.entry, "M": M, "H": H, "E": E, "K": wl.K,
          "rotating_sets": n_sets, "us_per_call": per_call, "kernel_us": kern,
+         "us_per_call_one_kernel": per_call_one, "kernel_us_one_kernel": kern_one,
          "tokens_per_s": M / (per_call * 1e-6), "alg_bytes": nbytes,
          "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
          "frac_hbm_kernel": nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBPS,
@@ -245,7 +254,7 @@ def measure_all(out_path=None):
 
     # few tokens through the 7168-wide router: split path (workspace) and
     # the single fused kernel, graph replay
-    for Ms in (1, 64, 1024, 4096):
+    for Ms in (1, 64, 1024, 2048, 4096):
         xs_ = hd[:Ms].contiguous()
         o_ = (torch.empty(Ms, wl.K, device=dev), torch.empty(Ms, wl.K, dtype=torch.int32,
                                                             device=dev))
@@ -259,6 +268,7 @@ def measure_all(out_path=None):
         t_one = graph_us(lambda st: fr_call(st, False))
         r = {"workload": "fused_router_h7168_few_tokens", "entry": wl.entry, "M": Ms, "H": H,
              "E": E, "K": wl.K, "splits": need // (4 * E * Ms) - 1 if need else 1,
+             "tile_rows": 64 if Ms > 2048 else 32,
              "us_per_call_graph_split": t_split, "us_per_call_graph_one_kernel": t_one}
         results.append(r)
         eprint(json.dumps(r))

@@ -150,8 +150,8 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *                  num_experts) bytes, 16-byte aligned, owned by the caller.
  *                  With NULL, or when that size is 0, one kernel computes
  *                  the projection and the routing and the logits never reach
- *                  memory.  Otherwise (fewer than 8192 tokens) the hidden
- *                  dimension is split over more workgroups: fp32 partial
+ *                  memory.  Otherwise (up to 8192 tokens, 256 experts) the
+ *                  hidden dimension is split over more workgroups: fp32 partial
  *                  logits and the summed logits go to the workspace, which
  *                  calls sharing it must not use at the same time.  The two
  *                  paths add the products in different orders, so their

@@ -50,11 +50,25 @@ constexpr int kFrWAhead = kFrWStages - 1;
 static_assert(kFrAAhead >= kFrWAhead, "hidden states run at least as far ahead as W");
 constexpr int kFrABytes = kFrRows * kFrBK * 2;  // 4 KiB: [32 rows][64 k] bf16, 128 B rows
 constexpr int kFrWBytes = kFrBK * kFrE * 2;     // 32 KiB: [64 k][256 experts] bf16, 512 B rows
-constexpr int kFrACopies = kFrABytes / 1024;                  // 4 wave loads per step
 constexpr int kFrWCopies = kFrWBytes / 1024 / kFrMathWaves;   // 8 per MFMA wave per step
 static_assert(2 * kFrRows * kFrE * 4 <= 2 * kFrWBytes, "epilogue reuses two W stages");
 static_assert(kFrAStages * kFrABytes + kFrWStages * kFrWBytes + kFrE * 4 <= 160 * 1024,
               "LDS of one workgroup");
+// A ring of a ROWS-row tile: 32 rows (the fused kernel, which also keeps
+// the bias in LDS) take 12 stages of 4 KiB; 64 rows (the partial kernel, no
+// bias) take 8 stages of 8 KiB, the rest of the 160 KiB beside the W ring.
+template <int ROWS> struct ARing {
+    static constexpr int kBytes = ROWS * kFrBK * 2;
+    static constexpr int kStages = ROWS == 32 ? 12 : 8;
+    static constexpr int kAhead = kStages - 1;
+    static constexpr int kCopies = kBytes / 1024;        // 4 or 8 wave loads per step
+    static_assert(kAhead >= kFrWAhead, "hidden states run at least as far ahead as W");
+    static_assert(kStages * kBytes + kFrWStages * kFrWBytes + (ROWS == 32 ? kFrE * 4 : 0) <=
+                      160 * 1024,
+                  "LDS of one workgroup");
+};
+static_assert(ARing<kFrRows>::kStages == kFrAStages && ARing<kFrRows>::kBytes == kFrABytes,
+              "the fused kernel's ring is the 32-row ring");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -106,11 +120,15 @@ __device__ __forceinline__ int w_swz(int k, int c) { return c ^ (4 * (k & 3)); }
 // hidden units each), in the MFMA layout the epilogues below unpack.  The
 // copy wave (its return value true) leaves acc alone.  Returns after every
 // copy has landed and a workgroup barrier, so the caller may reuse sA and sW.
+template <int ROWS>
 __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
                                            const uint16_t* __restrict__ w, int64_t M, int H,
                                            int64_t m0, int s_lo, int steps,
-                                           unsigned char (*sA)[kFrABytes],
-                                           unsigned char (*sW)[kFrWBytes], f32x16 (&acc)[2]) {
+                                           unsigned char (*sA)[ARing<ROWS>::kBytes],
+                                           unsigned char (*sW)[kFrWBytes],
+                                           f32x16 (&acc)[ROWS / 32][2]) {
+    using AR = ARing<ROWS>;
+    constexpr int MH = ROWS / 32;  // 32-row halves of the tile
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -119,17 +137,17 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
 
     // Direct-to-LDS copy assignment: every copy writes a 1 KiB block, lane l
     // its chunk l, and reads the global chunk that the swizzle puts there.
-    //   hidden-state wave: A block j (rows 8j .. 8j+7), j = 0..3; rows past M
-    //     read row M-1 (never stored);
+    //   hidden-state wave: A block j (rows 8j .. 8j+7), j < ROWS / 8; rows
+    //     past M read row M-1 (never stored);
     //   MFMA wave w: W blocks 8w .. 8w+7 (k rows 2b, 2b+1 of block b).
     // Hidden states come from HBM and W from L2.  Waits count a wave's own
     // loads in issue order, so a wave that copied both would wait on the slow
     // hidden-state loads whenever it needs a W tile; giving them to a wave of
     // their own lets each ring keep its own distance.
     const bool copier = wv == kFrMathWaves;
-    const uint16_t* a_src[kFrACopies];
+    const uint16_t* a_src[AR::kCopies];
 #pragma unroll
-    for (int j = 0; j < kFrACopies; ++j) {
+    for (int j = 0; j < AR::kCopies; ++j) {
         const int m = 8 * j + lane / 8;
         a_src[j] = hidden + min(m0 + m, M - 1) * H + 8 * a_swz(m, lane % 8);
     }
@@ -141,7 +159,7 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
     }
     auto issue_a = [&](int step, int stage) {
 #pragma unroll
-        for (int j = 0; j < kFrACopies; ++j)
+        for (int j = 0; j < AR::kCopies; ++j)
             lds_copy16(a_src[j] + step * kFrBK, lds_addr(sA[stage] + 1024 * j));
     };
     // W copies j0 .. j0+n-1 of a step.
@@ -152,13 +170,16 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
             lds_copy16(wk, w_off[j], lds_addr(sW[stage] + 1024 * (kFrWCopies * wv + j)));
     };
 
-    // Fragment addresses.  A: lane l reads row l%32, k chunk 2kk + l/32.
+    // Fragment addresses.  A (half mh): lane l reads row 32 mh + l%32, k chunk
+    // 2kk + l/32.
     // B (tile nt, k half h): lane l of 16-lane group g points at k row
     // 16kk + 8(g/2) + 4h + (l%16)/4 and experts n0 + 16(g%2) + 4(l%4) .. +3.
     const int fa_m = lane % 32;
     const int g = lane / 16, gi = lane % 16;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) { acc[0][q] = 0.f; acc[1][q] = 0.f; }
+    for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) { acc[mh][0][q] = 0.f; acc[mh][1][q] = 0.f; }
 
     // The MFMAs of one step.  All fragments of the step are read first (so
     // the LDS latency is paid once, not per k slice); before the MFMAs of k
@@ -166,11 +187,16 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
     // so that issuing them (the address unit takes a 1 KiB wave load every
     // 16 cycles) overlaps the math.
     auto compute = [&](const unsigned char* a_base, const unsigned char* w_base, auto copies) {
-        bf16x8 af[kFrBK / 16], bfr[kFrBK / 16][2];
+        bf16x8 af[MH][kFrBK / 16], bfr[kFrBK / 16][2];
 #pragma unroll
         for (int kk = 0; kk < kFrBK / 16; ++kk) {
             const int ac = 2 * kk + lane / 32;
-            af[kk] = *reinterpret_cast<const bf16x8*>(a_base + fa_m * 128 + 16 * a_swz(fa_m, ac));
+#pragma unroll
+            for (int mh = 0; mh < MH; ++mh) {
+                const int m = 32 * mh + fa_m;
+                af[mh][kk] = *reinterpret_cast<const bf16x8*>(a_base + m * 128 +
+                                                              16 * a_swz(m, ac));
+            }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const int e = wv * 64 + nt * 32 + 16 * (g % 2) + 4 * (gi % 4);
@@ -190,30 +216,32 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
         for (int kk = 0; kk < kFrBK / 16; ++kk) {
             copies(kk);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk][nt], acc[nt], 0,
-                                                                  0, 0);
+            for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mh][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[mh][kk], bfr[kk][nt], acc[mh][nt], 0, 0, 0);
         }
     };
 
     // Rings.  At step s the hidden-state wave issues the copies of step
-    // s + kFrAAhead and each MFMA wave those of W for step s + kFrWAhead (spread
+    // s + AR::kAhead and each MFMA wave those of W for step s + kFrWAhead (spread
     // over its MFMAs); the prologues issue what the steps before step 0 would
     // have.  At the top of step s a wave's loads issued after those of step s
-    // belong to the kFrAAhead - 1 (kFrWAhead - 1) later steps, so waiting until
+    // belong to the AR::kAhead - 1 (kFrWAhead - 1) later steps, so waiting until
     // at most that many remain completes step s.  The barrier then makes every
     // wave's copies visible and retires the reads of step s-1, whose stages the
     // copies of step s reuse.  Copies past the last step repeat it into a stage
     // that is never read again, so the count in flight is the same at every
     // step.  Both kinds of wave pass the same number of barriers.
     if (copier) {
-        for (int q = 0; q < kFrAAhead; ++q) issue_a(min(q, steps - 1), q);
+        for (int q = 0; q < AR::kAhead; ++q) issue_a(min(q, steps - 1), q);
         int ia = 0;
         for (int s = 0; s < steps; ++s) {
-            wait_vmcnt<kFrACopies * (kFrAAhead - 1)>();
+            wait_vmcnt<AR::kCopies * (AR::kAhead - 1)>();
             barrier_no_fence();
-            issue_a(min(s + kFrAAhead, steps - 1), ia == 0 ? kFrAStages - 1 : ia - 1);
-            ia = ia == kFrAStages - 1 ? 0 : ia + 1;
+            issue_a(min(s + AR::kAhead, steps - 1), ia == 0 ? AR::kStages - 1 : ia - 1);
+            ia = ia == AR::kStages - 1 ? 0 : ia + 1;
         }
     } else {
         for (int q = 0; q < kFrWAhead; ++q) issue_w(min(q, steps - 1), q, 0, kFrWCopies);
@@ -226,7 +254,7 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
             compute(sA[ia], sW[iw], [&](int kk) {
                 issue_w(w_step, w_stage, kk * kFrWCopies / 4, kFrWCopies / 4);
             });
-            ia = ia == kFrAStages - 1 ? 0 : ia + 1;
+            ia = ia == AR::kStages - 1 ? 0 : ia + 1;
             iw = iw == kFrWStages - 1 ? 0 : iw + 1;
         }
     }
@@ -248,8 +276,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const int lane = t % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
     const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
-    f32x16 acc[2];
-    const bool copier = fr_project(hidden, w, M, H, m0, 0, H / kFrBK, sA, sW, acc);
+    f32x16 acc[1][2];
+    const bool copier = fr_project<kFrRows>(hidden, w, M, H, m0, 0, H / kFrBK, sA, sW, acc);
 
     // ---- epilogue: logits to LDS, then route the 32 rows (8 lanes per row)
     float* L = reinterpret_cast<float*>(sW[0]);  // [32][256] fp32 logits
@@ -261,7 +289,7 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
         for (int j = 0; j < 16; ++j) {
             const int m = 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
             // soft-capping (cap != 0): every consumer below sees capped logits
-            L[m * kFrE + n] = cap != 0.0f ? cap * tanh_f32(acc[nt][j] / cap) : acc[nt][j];
+            L[m * kFrE + n] = cap != 0.0f ? cap * tanh_f32(acc[0][nt][j] / cap) : acc[0][nt][j];
         }
     }
     if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
@@ -294,39 +322,44 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
         id_out, [&](int e) { return lrow[e]; });
 }
 
-// ---- few tokens: the hidden dimension split over workgroups
+// ---- up to 8192 tokens: the hidden dimension split over workgroups
 //
 // With fewer than 256 row tiles the single kernel leaves compute units idle
-// and each workgroup walks all of H one W tile after the other.  The split
-// path gives workgroup (tile, s) the hidden steps of split s only; it writes
-// its fp32 partial logits to part[s][M][256].  A second kernel sums the
-// splits of each logit in a fixed order (so results do not depend on timing)
-// and soft-caps the sum, and the standalone routing kernel routes the fp32
-// logits.
+// and each workgroup walks all of H one W tile after the other; and every
+// workgroup streams all of W for its 32 tokens.  The split path gives
+// workgroup (tile, s) the hidden steps of split s only, on tiles of 32 or 64
+// tokens (64: W is streamed once per 64 tokens); it writes its fp32 partial
+// logits to part[s][M][256].  A second kernel sums the splits of each logit
+// in a fixed order (so results do not depend on timing) and soft-caps the
+// sum, and the standalone routing kernel routes the fp32 logits.
+template <int ROWS>
 __global__ __launch_bounds__(kFrThreads) void fused_router_partial_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w, int64_t M, int H,
     int nsplit, float* __restrict__ part) {
-    __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
+    using AR = ARing<ROWS>;
+    __shared__ __align__(1024) unsigned char sA[AR::kStages][AR::kBytes];
     __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
 
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
+    const int64_t m0 = (int64_t)blockIdx.x * ROWS;
     const int split = blockIdx.y, steps_all = H / kFrBK;
     const int s_lo = split * steps_all / nsplit, s_hi = (split + 1) * steps_all / nsplit;
-    f32x16 acc[2];
-    if (fr_project(hidden, w, M, H, m0, s_lo, s_hi - s_lo, sA, sW, acc)) return;
+    f32x16 acc[ROWS / 32][2];
+    if (fr_project<ROWS>(hidden, w, M, H, m0, s_lo, s_hi - s_lo, sA, sW, acc)) return;
 
     float* out = part + (int64_t)split * M * kFrE;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int n = wv * 64 + nt * 32 + (lane % 32);
+    for (int mh = 0; mh < ROWS / 32; ++mh)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int64_t row = m0 + 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
-            if (row < M) out[row * kFrE + n] = acc[nt][j];
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = wv * 64 + nt * 32 + (lane % 32);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t row = m0 + 32 * mh + 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
+                if (row < M) out[row * kFrE + n] = acc[mh][nt][j];
+            }
         }
-    }
 }
 
 // logits[m][e] = sum of part[s][m][e] over the splits, then the soft cap.
@@ -368,14 +401,20 @@ __global__ __launch_bounds__(1024) void fr_reduce_kernel(const float* __restrict
     reinterpret_cast<float4*>(logits)[row * 64 + c4] = a;
 }
 
-route_status_t launch_split(const FusedProblem& f, int nsplit) {
+route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
     const RouteProblem& p = f.route;
-    const int64_t tiles = (f.M + kFrRows - 1) / kFrRows;
+    const int nsplit = plan.splits;
+    const int64_t tiles = (f.M + plan.rows - 1) / plan.rows;
     float* part = f.workspace;
     float* logits = part + (int64_t)nsplit * f.M * kFrE;
-    hipLaunchKernelGGL(fused_router_partial_kernel, dim3((unsigned)tiles, (unsigned)nsplit),
-                       dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
-                       static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
+    if (plan.rows == 64)
+        hipLaunchKernelGGL(fused_router_partial_kernel<64>, dim3((unsigned)tiles, (unsigned)nsplit),
+                           dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                           static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
+    else
+        hipLaunchKernelGGL(fused_router_partial_kernel<32>, dim3((unsigned)tiles, (unsigned)nsplit),
+                           dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                           static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
     if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
     const int S = nsplit >= 16 ? 16 : nsplit >= 8 ? 8 : nsplit >= 4 ? 4 : 2;
     const dim3 rgrid((unsigned)((f.M + 16 / S - 1) / (16 / S)));
@@ -429,22 +468,26 @@ bool fused_router_supported(const FusedProblem& f) {
     return !(p.scoring == ROUTE_SOFTMAX && p.rule == ROUTE_GROUP_TOP2_SUM);
 }
 
-int fused_router_splits(int64_t M, int H) {
+SplitPlan fused_router_split_plan(int64_t M, int H) {
     // One workgroup fills a compute unit (its LDS), so up to 256 workgroups
-    // run in one round.  Split as far as one round allows, then back off to
-    // the fewest splits that keep the same steps per workgroup (every split
-    // costs partial-logit traffic).  From 129 row tiles on no split fits.
-    const int64_t tiles = (M + kFrRows - 1) / kFrRows;
+    // run in one round.  Above 2048 tokens the partial kernel takes tiles of
+    // 64 rows: each workgroup streams W once for twice the tokens.  Split as
+    // far as one round allows, then back off to the fewest splits that keep
+    // the same steps per workgroup (every split costs partial-logit
+    // traffic).  From 129 tiles on no split fits and the single fused kernel
+    // runs.
+    const int rows = M > 2048 ? 64 : 32;
+    const int64_t tiles = (M + rows - 1) / rows;
     const int steps = H / kFrBK;
-    if (M <= 0 || steps < 2) return 1;
+    if (M <= 0 || steps < 2) return {kFrRows, 1};
     const int64_t most = std::min<int64_t>(steps, 256 / tiles);
-    if (most < 2) return 1;
+    if (most < 2) return {kFrRows, 1};
     const int per_split = (steps + (int)most - 1) / (int)most;
-    return (steps + per_split - 1) / per_split;
+    return {rows, (steps + per_split - 1) / per_split};
 }
 
 size_t fused_router_workspace_bytes(int64_t M, int H) {
-    const int n = fused_router_splits(M, H);
+    const int n = fused_router_split_plan(M, H).splits;
     return n == 1 ? 0 : sizeof(float) * kFrE * (size_t)M * (size_t)(n + 1);
 }
 
@@ -452,8 +495,8 @@ route_status_t launch_fused_router(const FusedProblem& f) {
     const RouteProblem& p = f.route;
     if (p.E != kFrE) return launch_small_router(f);
     if (f.workspace != nullptr) {
-        const int nsplit = fused_router_splits(f.M, f.H);
-        if (nsplit > 1) return launch_split(f, nsplit);
+        const SplitPlan plan = fused_router_split_plan(f.M, f.H);
+        if (plan.splits > 1) return launch_split(f, plan);
     }
     const bool soft = p.scoring == ROUTE_SOFTMAX;
     const bool bias = p.bias != nullptr;

@@ -61,7 +61,11 @@ route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
 bool small_router_supported(const FusedProblem& p);  // E = 8 or 16 (fused_router_small.hip)
 route_status_t launch_small_router(const FusedProblem& p);
-int fused_router_splits(int64_t M, int H);  // hidden-dimension splits (1: one kernel)
+struct SplitPlan {
+    int rows;    // tokens per tile of the partial kernel (32 or 64)
+    int splits;  // hidden-dimension splits; 1: the single fused kernel
+};
+SplitPlan fused_router_split_plan(int64_t M, int H);
 size_t fused_router_workspace_bytes(int64_t M, int H);
 size_t dispatch_workspace_bytes(int64_t n, int E);
 route_status_t launch_dispatch(const DispatchProblem& d);

@@ -107,6 +107,8 @@ def test_fused_router_one_lane_holds_most_picks(G, TG):
     (300, 640, 8, 3, 6, "softmax", "max", False, False, 0.0),       # 10 tiles, softmax
     (1000, 384, 1, 1, 2, "softmax", "max", False, False, 30.0),     # top-2 softmax, capped
     (130, 7168, 8, 4, 8, "sigmoid", "top2sum", True, True, 2.0),    # saturating cap
+    (3000, 640, 8, 4, 8, "sigmoid", "top2sum", True, True, 0.0),    # 64-row tiles, ragged
+    (2100, 1024, 1, 1, 2, "softmax", "max", False, False, 30.0),    # 64-row tiles, capped
 ])
 def test_fused_router_split_path(M, H, G, TG, K, scoring, rule, bias, renorm, cap):
     """Few tokens: the hidden dimension is split over workgroups, partial
@@ -133,14 +135,16 @@ def test_fused_router_split_path(M, H, G, TG, K, scoring, rule, bias, renorm, ca
     assert rep1.ok(), rep1.summary()
 
 
-def test_fused_router_split_path_full_width_sampled():
-    """128 row tiles of the 7168-wide router: two splits of 56 steps."""
+@pytest.mark.parametrize("M,splits", [(4096, 4), (8192, 2)])
+def test_fused_router_split_path_full_width_sampled(M, splits):
+    """64-row tiles of the 7168-wide router: 4 splits of 28 steps at 4096
+    tokens, 2 of 56 at 8192 (the full workload)."""
     wl = WORKLOADS["fused_router_h7168"]
-    M = 4096
-    assert mr.route_fused_router_workspace_size(M, wl.hidden_dim, wl.E) == 4 * 256 * M * 3
+    assert mr.route_fused_router_workspace_size(M, wl.hidden_dim, wl.E) == \
+        4 * 256 * M * (splits + 1)
     hidden, w = make_router_inputs(wl, M)
     b = make_bias(wl)
-    log(f"[gpu] route_fused_router split path M={M} H={wl.hidden_dim} (2 splits)")
+    log(f"[gpu] route_fused_router split path M={M} H={wl.hidden_dim} ({splits} splits)")
     wt, ids = _run(hidden, w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
     rng = np.random.default_rng(11)
     rows = np.unique(np.concatenate([np.arange(40), np.arange(M - 40, M),
@@ -165,11 +169,13 @@ def test_fused_router_split_path_deterministic_and_reused_workspace():
 
 
 def test_fused_router_full_workload_sampled():
+    """The single fused kernel (no workspace) on the full 8192-token workload."""
     wl = WORKLOADS["fused_router_h7168"]
     hidden, w = make_router_inputs(wl)
     b = make_bias(wl)
-    log(f"[gpu] route_fused_router workload={wl.name} M={wl.M} H={wl.hidden_dim}")
-    wt, ids = _run(hidden, w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
+    log(f"[gpu] route_fused_router workload={wl.name} M={wl.M} H={wl.hidden_dim} one kernel")
+    wt, ids = _run(hidden, w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum",
+                   workspace=False)
     # oracle on sampled rows: both ends of the batch, block boundaries, random
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.arange(40), np.arange(wl.M - 40, wl.M),
