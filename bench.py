@@ -273,11 +273,13 @@ def measure_all(out_path=None):
         results.append(r)
         eprint(json.dumps(r))
 
-    # few experts: 8-expert router, hidden 4096, top-2 softmax, cap 30
-    wl8 = WORKLOADS["fused_router_e8_h4096"]
-    h8, w8 = make_router_inputs(wl8)
-    h8d, w8d = dev_tensor(h8), dev_tensor(w8)
-    for Ms in (1, 64, 2048, wl8.M):
+    # few experts: 8-expert router (hidden 4096, top-2 softmax, cap 30) and
+    # 16-expert router (hidden 6144, top-4 softmax, renormalised)
+    for wl8, Ms in [(WORKLOADS[n], m) for n in ("fused_router_e8_h4096", "fused_router_e16_h6144")
+                    for m in (1, 64, 2048, 8192)]:
+        if Ms == 1:
+            h8, w8 = make_router_inputs(wl8)
+            h8d, w8d = dev_tensor(h8), dev_tensor(w8)
         xs_ = h8d[:Ms].contiguous()
         o_ = (torch.empty(Ms, wl8.K, device=dev), torch.empty(Ms, wl8.K, dtype=torch.int32,
                                                              device=dev))

@@ -87,6 +87,11 @@ WORKLOADS = {
                                       M=8192, E=8, K=2, scoring="softmax", renormalize=False,
                                       dtype="bf16", hidden_dim=4096, w_std=(1.0 / 4096) ** 0.5,
                                       softcap=30.0),
+    # 16 experts (DBRX-like: hidden 6144, top-4 softmax, renormalised).
+    "fused_router_e16_h6144": Workload("fused_router_e16_h6144", "route_fused_router",
+                                       M=8192, E=16, K=4, scoring="softmax", renormalize=True,
+                                       dtype="bf16", hidden_dim=6144,
+                                       w_std=(1.0 / 6144) ** 0.5),
 }
 
 BIASED_GROUPED_M_SWEEP = (1, 4, 16, 64, 128, 1024, 8192, 65536)
