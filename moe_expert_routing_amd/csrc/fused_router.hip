@@ -401,6 +401,101 @@ __global__ __launch_bounds__(1024) void fr_reduce_kernel(const float* __restrict
     reinterpret_cast<float4*>(logits)[row * 64 + c4] = a;
 }
 
+// Few tokens (many splits): one row per block.  The splits are summed as
+// fr_reduce_kernel<16> sums them (slice q adds splits q, q + 16, ...; the
+// slices in order), soft-capped, and the first wave routes the row with the
+// fused kernel's epilogue (its other 7 row slots are computed, never stored).
+// This saves the logits' round trip through memory and one launch.
+template <bool SOFTMAX, bool BIAS, int GRP>
+__global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
+    const float* __restrict__ part, int64_t M, int nsplit, float cap,
+    const float* __restrict__ bias, int TG, int K, int renorm, float* __restrict__ w_out,
+    int32_t* __restrict__ id_out) {
+    __shared__ float4 red[16][64];
+    __shared__ __align__(16) float L[kFrE];         // the row's logits
+    __shared__ __align__(16) float S[8][kFrE];      // routing scratch of the wave's 8 row slots
+    __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
+
+    const int t = threadIdx.x, c4 = t % 64, q = t / 64;
+    const int64_t row = blockIdx.x;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4* src = reinterpret_cast<const float4*>(part) + row * 64 + c4;
+    const int64_t split_stride = M * 64;
+#pragma unroll 4
+    for (int sp = q; sp < nsplit; sp += 16) {
+        const float4 v = src[sp * split_stride];
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    red[q][c4] = a;
+    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
+    __syncthreads();
+    if (q == 0) {
+#pragma unroll
+        for (int j = 1; j < 16; ++j) {
+            const float4 v = red[j][c4];
+            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+        if (cap != 0.0f) {
+            a.x = cap * tanh_f32(a.x / cap);
+            a.y = cap * tanh_f32(a.y / cap);
+            a.z = cap * tanh_f32(a.z / cap);
+            a.w = cap * tanh_f32(a.w / cap);
+        }
+        reinterpret_cast<float4*>(L)[c4] = a;
+    }
+    __syncthreads();
+    if (t >= kWave) return;
+
+    const int sub = t % 8, rw = t / 8;
+    KeyParams kp;
+    if constexpr (BIAS) {
+        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            bmin = fminf(bmin, s_bias[sub * 32 + j]);
+            bmax = fmaxf(bmax, s_bias[sub * 32 + j]);
+        }
+        kp = key_params(row_min<8>(bmin), 1.0f + row_max<8>(bmax));
+    } else {
+        kp = key_params(0.0f, 1.0f);
+    }
+    float x[32];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const float4 d = reinterpret_cast<const float4*>(L + sub * 32)[v];
+        x[4 * v] = d.x; x[4 * v + 1] = d.y; x[4 * v + 2] = d.z; x[4 * v + 3] = d.w;
+    }
+    route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
+        x, sub, rw, rw == 0, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
+        [&](int e) { return L[e]; });
+}
+
+template <bool SOFTMAX, bool BIAS, int GRP>
+route_status_t launch_rr(const FusedProblem& f, const float* part, int nsplit) {
+    const RouteProblem& p = f.route;
+    hipLaunchKernelGGL((fr_reduce_route_kernel<SOFTMAX, BIAS, GRP>), dim3((unsigned)f.M),
+                       dim3(1024), 0, p.stream, part, f.M, nsplit, f.softcap, p.bias, p.TG, p.K,
+                       p.renorm ? 1 : 0, p.weights, p.ids);
+    return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
+}
+
+route_status_t launch_reduce_route(const FusedProblem& f, const float* part, int nsplit) {
+    const RouteProblem& p = f.route;
+    const bool soft = p.scoring == ROUTE_SOFTMAX;
+    const bool bias = p.bias != nullptr;
+    if (p.G == 1) {
+        if (soft) return launch_rr<true, false, 0>(f, part, nsplit);
+        return bias ? launch_rr<false, true, 0>(f, part, nsplit)
+                    : launch_rr<false, false, 0>(f, part, nsplit);
+    }
+    if (p.rule == ROUTE_GROUP_TOP2_SUM)
+        return bias ? launch_rr<false, true, 2>(f, part, nsplit)
+                    : launch_rr<false, false, 2>(f, part, nsplit);
+    if (soft) return launch_rr<true, false, 1>(f, part, nsplit);
+    return bias ? launch_rr<false, true, 1>(f, part, nsplit)
+                : launch_rr<false, false, 1>(f, part, nsplit);
+}
+
 route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
     const RouteProblem& p = f.route;
     const int nsplit = plan.splits;
@@ -416,6 +511,8 @@ route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
                            static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
     if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
+    // up to 256 tokens (16+ splits): sum and route in one kernel, a row per block
+    if (f.M <= 256 && nsplit >= 16) return launch_reduce_route(f, part, nsplit);
     const int S = nsplit >= 16 ? 16 : nsplit >= 8 ? 8 : nsplit >= 4 ? 4 : 2;
     const dim3 rgrid((unsigned)((f.M + 16 / S - 1) / (16 / S)));
     switch (S) {
