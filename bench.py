@@ -214,11 +214,22 @@ def measure_all(out_path=None):
     per_call, kern = time_calls(launch_fr, n_sets, stream, steps=200, warmup=20)
     per_call_one, kern_one = time_calls(lambda i: launch_fr(i, False), n_sets, stream,
                                         steps=200, warmup=20)
+    # context: the unfused pair, torch's bf16 matmul (hipBLASLt) to bf16
+    # logits, then the routing kernel
+    lgs = [torch.empty(M, E, dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+
+    def launch_unfused(i):
+        with torch.cuda.stream(stream):
+            torch.matmul(hs[i], wd, out=lgs[i])
+        mr.route_biased_grouped_topk(lgs[i], bd, wl.K, wl.G, wl.TG, wl.renormalize,
+                                     outs[i][0], outs[i][1], stream=stream)
+    per_call_unfused, _ = time_calls(launch_unfused, n_sets, stream, steps=100, warmup=10)
     nbytes = M * H * 2 + H * E * 2 + E * 4 + M * wl.K * 8
     flops = 2.0 * M * H * E
     r = {"workload": wl.name, "entry": wl.entry, "M": M, "H": H, "E": E, "K": wl.K,
          "rotating_sets": n_sets, "us_per_call": per_call, "kernel_us": kern,
          "us_per_call_one_kernel": per_call_one, "kernel_us_one_kernel": kern_one,
+         "us_per_call_torch_matmul_then_routing": per_call_unfused,
          "tokens_per_s": M / (per_call * 1e-6), "alg_bytes": nbytes,
          "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
          "frac_hbm_kernel": nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBPS,
@@ -266,10 +277,18 @@ def measure_all(out_path=None):
                                   "top2sum", o_[0], o_[1], stream=st, workspace=ws_arg)
         t_split = graph_us(lambda st: fr_call(st, wsp))
         t_one = graph_us(lambda st: fr_call(st, False))
+        lg_ = torch.empty(Ms, E, dtype=torch.bfloat16, device=dev)
+
+        def unfused_few(st):
+            torch.matmul(xs_, wd, out=lg_)
+            mr.route_biased_grouped_topk(lg_, bd, wl.K, wl.G, wl.TG, wl.renormalize, o_[0],
+                                         o_[1], stream=st)
+        t_unfused = graph_us(unfused_few)
         r = {"workload": "fused_router_h7168_few_tokens", "entry": wl.entry, "M": Ms, "H": H,
              "E": E, "K": wl.K, "splits": need // (4 * E * Ms) - 1 if need else 1,
              "tile_rows": 64 if Ms > 2048 else 32,
-             "us_per_call_graph_split": t_split, "us_per_call_graph_one_kernel": t_one}
+             "us_per_call_graph_split": t_split, "us_per_call_graph_one_kernel": t_one,
+             "us_per_call_graph_torch_matmul_then_routing": t_unfused}
         results.append(r)
         eprint(json.dumps(r))
 
