@@ -285,7 +285,7 @@ def measure_all(out_path=None):
                                          o_[1], stream=st)
         t_unfused = graph_us(unfused_few)
         r = {"workload": "fused_router_h7168_few_tokens", "entry": wl.entry, "M": Ms, "H": H,
-             "E": E, "K": wl.K, "splits": need // (4 * E * Ms) - 1 if need else 1,
+             "E": E, "K": wl.K, "splits": need // (4 * E * Ms) if need else 1,
              "tile_rows": 64 if Ms > 2048 else 32,
              "us_per_call_graph_split": t_split, "us_per_call_graph_one_kernel": t_one,
              "us_per_call_graph_torch_matmul_then_routing": t_unfused}

@@ -151,9 +151,9 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *                  With NULL, or when that size is 0, one kernel computes
  *                  the projection and the routing and the logits never reach
  *                  memory.  Otherwise (up to 8192 tokens, 256 experts) the
- *                  hidden dimension is split over more workgroups: fp32 partial
- *                  logits and the summed logits go to the workspace, which
- *                  calls sharing it must not use at the same time.  The two
+ *                  hidden dimension is split over more workgroups: their
+ *                  fp32 partial logits go to the workspace, which calls
+ *                  sharing it must not use at the same time.  The two
  *                  paths add the products in different orders, so their
  *                  logits may differ in the last bits.
  * Compiled range, with hidden_states and router_weight 16-byte aligned:

@@ -330,8 +330,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
 // workgroup (tile, s) the hidden steps of split s only, on tiles of 32 or 64
 // tokens (64: W is streamed once per 64 tokens); it writes its fp32 partial
 // logits to part[s][M][256].  A second kernel sums the splits of each logit
-// in a fixed order (so results do not depend on timing) and soft-caps the
-// sum, and the standalone routing kernel routes the fp32 logits.
+// in a fixed order (so results do not depend on timing), soft-caps the sum
+// and routes the row; the summed logits never reach memory.
 template <int ROWS>
 __global__ __launch_bounds__(kFrThreads) void fused_router_partial_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w, int64_t M, int H,
@@ -362,50 +362,11 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_partial_kernel(
         }
 }
 
-// logits[m][e] = sum of part[s][m][e] over the splits, then the soft cap.
-// A block holds 1024 threads: 64 float4 columns x S split slices x 16/S
-// rows.  Slice q sums splits q, q+S, q+2S, ... in that order; slice sums are
-// then added in slice order.
-template <int S>
-__global__ __launch_bounds__(1024) void fr_reduce_kernel(const float* __restrict__ part,
-                                                         int64_t M, int nsplit, float cap,
-                                                         float* __restrict__ logits) {
-    constexpr int R = 16 / S;
-    __shared__ float4 red[S][R][64];
-    const int c4 = threadIdx.x % 64, q = (threadIdx.x / 64) % S, r = threadIdx.x / (64 * S);
-    const int64_t row = (int64_t)blockIdx.x * R + r;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < M) {
-        const float4* src = reinterpret_cast<const float4*>(part) + row * 64 + c4;
-        const int64_t split_stride = M * 64;
-#pragma unroll 4
-        for (int sp = q; sp < nsplit; sp += S) {
-            const float4 v = src[sp * split_stride];
-            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-        }
-    }
-    red[q][r][c4] = a;
-    __syncthreads();
-    if (q != 0 || row >= M) return;
-#pragma unroll
-    for (int j = 1; j < S; ++j) {
-        const float4 v = red[j][r][c4];
-        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
-    }
-    if (cap != 0.0f) {
-        a.x = cap * tanh_f32(a.x / cap);
-        a.y = cap * tanh_f32(a.y / cap);
-        a.z = cap * tanh_f32(a.z / cap);
-        a.w = cap * tanh_f32(a.w / cap);
-    }
-    reinterpret_cast<float4*>(logits)[row * 64 + c4] = a;
-}
-
-// Few tokens (many splits): one row per block.  The splits are summed as
-// fr_reduce_kernel<16> sums them (slice q adds splits q, q + 16, ...; the
-// slices in order), soft-capped, and the first wave routes the row with the
-// fused kernel's epilogue (its other 7 row slots are computed, never stored).
-// This saves the logits' round trip through memory and one launch.
+// Many splits (8 or more): one row per block of 1024 threads, 64 float4
+// columns x 16 split slices.  Slice q adds splits q, q + 16, ... in that
+// order and the slice sums are added in slice order; the sum is soft-capped
+// and the first wave routes the row with the fused kernel's epilogue (its
+// other 7 row slots are computed, never stored).
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     const float* __restrict__ part, int64_t M, int nsplit, float cap,
@@ -470,12 +431,85 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
         [&](int e) { return L[e]; });
 }
 
+// Otherwise a wave per 8 rows, in the routing kernel's layout: lane sub of
+// row rw adds its 32 logits over the splits in split order, soft-caps them
+// and the wave routes its rows with the fused kernel's epilogue.  Rows past
+// M read row M-1 and are never stored.
+template <bool SOFTMAX, bool BIAS, int GRP>
+__global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
+    const float* __restrict__ part, int64_t M, int nsplit, float cap,
+    const float* __restrict__ bias, int TG, int K, int renorm, float* __restrict__ w_out,
+    int32_t* __restrict__ id_out) {
+    __shared__ __align__(16) float S[8][kFrE];      // routing scratch of the 8 rows
+    __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
+
+    const int t = threadIdx.x, sub = t % 8, rw = t / 8;
+    const int64_t row = (int64_t)blockIdx.x * 8 + rw;
+    const int64_t rrow = row < M ? row : M - 1;
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int i = t; i < kFrE; i += kWave) s_bias[bias_elem<kFrE>(i)] = bias[i];
+    }
+    const int64_t split_stride = M * kFrE;
+    const float* src = part + rrow * kFrE + sub * 32;
+    float x[32];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const float4 d = reinterpret_cast<const float4*>(src)[v];
+        x[4 * v] = d.x; x[4 * v + 1] = d.y; x[4 * v + 2] = d.z; x[4 * v + 3] = d.w;
+    }
+#pragma unroll 4
+    for (int sp = 1; sp < nsplit; ++sp) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float4 d = reinterpret_cast<const float4*>(src + sp * split_stride)[v];
+            x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
+        }
+    }
+    if (cap != 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) x[j] = cap * tanh_f32(x[j] / cap);
+    }
+    __syncthreads();
+
+    KeyParams kp;
+    if constexpr (BIAS) {
+        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            bmin = fminf(bmin, s_bias[sub * 32 + j]);
+            bmax = fmaxf(bmax, s_bias[sub * 32 + j]);
+        }
+        kp = key_params(row_min<8>(bmin), 1.0f + row_max<8>(bmax));
+    } else {
+        kp = key_params(0.0f, 1.0f);
+    }
+    // the logit of expert e, recomputed in the same order (rare paths only)
+    const float* rsrc = part + rrow * kFrE;
+    route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
+        x, sub, rw, row < M, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
+        [&](int e) {
+            float v = rsrc[e];
+            for (int sp = 1; sp < nsplit; ++sp) v += rsrc[sp * split_stride + e];
+            return cap != 0.0f ? cap * tanh_f32(v / cap) : v;
+        });
+}
+
 template <bool SOFTMAX, bool BIAS, int GRP>
 route_status_t launch_rr(const FusedProblem& f, const float* part, int nsplit) {
     const RouteProblem& p = f.route;
-    hipLaunchKernelGGL((fr_reduce_route_kernel<SOFTMAX, BIAS, GRP>), dim3((unsigned)f.M),
-                       dim3(1024), 0, p.stream, part, f.M, nsplit, f.softcap, p.bias, p.TG, p.K,
-                       p.renorm ? 1 : 0, p.weights, p.ids);
+    // 8+ splits (up to 1024 tokens of a 7168-wide router): a block per row
+    // sums them 16 wide; fewer splits: a wave per 8 rows, each lane adding
+    // its logits over the splits
+    if (nsplit >= 8)
+        hipLaunchKernelGGL((fr_reduce_route_kernel<SOFTMAX, BIAS, GRP>), dim3((unsigned)f.M),
+                           dim3(1024), 0, p.stream, part, f.M, nsplit, f.softcap, p.bias, p.TG,
+                           p.K, p.renorm ? 1 : 0, p.weights, p.ids);
+    else
+        hipLaunchKernelGGL((fr_reduce_route_rows_kernel<SOFTMAX, BIAS, GRP>),
+                           dim3((unsigned)((f.M + 7) / 8)), dim3(kWave), 0, p.stream, part, f.M,
+                           nsplit, f.softcap, p.bias, p.TG, p.K, p.renorm ? 1 : 0, p.weights,
+                           p.ids);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 
@@ -500,8 +534,7 @@ route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
     const RouteProblem& p = f.route;
     const int nsplit = plan.splits;
     const int64_t tiles = (f.M + plan.rows - 1) / plan.rows;
-    float* part = f.workspace;
-    float* logits = part + (int64_t)nsplit * f.M * kFrE;
+    float* part = f.workspace;  // [nsplit][M][256] fp32
     if (plan.rows == 64)
         hipLaunchKernelGGL(fused_router_partial_kernel<64>, dim3((unsigned)tiles, (unsigned)nsplit),
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
@@ -511,32 +544,7 @@ route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
                            static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
     if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
-    // up to 256 tokens (16+ splits): sum and route in one kernel, a row per block
-    if (f.M <= 256 && nsplit >= 16) return launch_reduce_route(f, part, nsplit);
-    const int S = nsplit >= 16 ? 16 : nsplit >= 8 ? 8 : nsplit >= 4 ? 4 : 2;
-    const dim3 rgrid((unsigned)((f.M + 16 / S - 1) / (16 / S)));
-    switch (S) {
-        case 16:
-            hipLaunchKernelGGL(fr_reduce_kernel<16>, rgrid, dim3(1024), 0, p.stream, part, f.M,
-                               nsplit, f.softcap, logits);
-            break;
-        case 8:
-            hipLaunchKernelGGL(fr_reduce_kernel<8>, rgrid, dim3(1024), 0, p.stream, part, f.M,
-                               nsplit, f.softcap, logits);
-            break;
-        case 4:
-            hipLaunchKernelGGL(fr_reduce_kernel<4>, rgrid, dim3(1024), 0, p.stream, part, f.M,
-                               nsplit, f.softcap, logits);
-            break;
-        default:
-            hipLaunchKernelGGL(fr_reduce_kernel<2>, rgrid, dim3(1024), 0, p.stream, part, f.M,
-                               nsplit, f.softcap, logits);
-    }
-    if (hipGetLastError() != hipSuccess) return ROUTE_ELAUNCH;
-    RouteProblem rp = p;
-    rp.logits = logits;
-    rp.dtype = ROUTE_F32;
-    return launch_route(rp);
+    return launch_reduce_route(f, part, nsplit);
 }
 
 template <bool SOFTMAX, bool BIAS, int GRP>
@@ -585,7 +593,7 @@ SplitPlan fused_router_split_plan(int64_t M, int H) {
 
 size_t fused_router_workspace_bytes(int64_t M, int H) {
     const int n = fused_router_split_plan(M, H).splits;
-    return n == 1 ? 0 : sizeof(float) * kFrE * (size_t)M * (size_t)(n + 1);
+    return n == 1 ? 0 : sizeof(float) * kFrE * (size_t)M * (size_t)n;
 }
 
 route_status_t launch_fused_router(const FusedProblem& f) {

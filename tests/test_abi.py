@@ -152,19 +152,19 @@ def test_fused_router_workspace_size():
     assert ws(1, 64, 256) == 0            # one hidden step: nothing to split
     assert ws(8193, 7168, 256) == 0       # 129 tiles of 64: no split fits one round
     assert ws(65536, 7168, 256) == 0
-    # fp32 partials of every split plus the summed logits, [M][256] each.
+    # fp32 partials of every split, [M][256] each.
     # Up to 2048 tokens, tiles of 32 rows.  One tile and 112 steps of 64:
     # 112 splits of one step.
-    assert ws(1, 7168, 256) == 4 * 256 * 1 * 113
-    assert ws(32, 7168, 256) == 4 * 256 * 32 * 113
+    assert ws(1, 7168, 256) == 4 * 256 * 1 * 112
+    assert ws(32, 7168, 256) == 4 * 256 * 32 * 112
     # 3 tiles: 56 splits of two steps (168 workgroups, one round)
-    assert ws(65, 7168, 256) == 4 * 256 * 65 * 57
+    assert ws(65, 7168, 256) == 4 * 256 * 65 * 56
     # above 2048 tokens, tiles of 64 rows: 43 tiles -> 5 splits of 23 steps
-    assert ws(2720, 7168, 256) == 4 * 256 * 2720 * 6
+    assert ws(2720, 7168, 256) == 4 * 256 * 2720 * 5
     # 64 tiles: 4 splits of 28 steps; 65 tiles: 3 of 38; 128 tiles: 2 of 56
-    assert ws(4096, 7168, 256) == 4 * 256 * 4096 * 5
-    assert ws(4097, 7168, 256) == 4 * 256 * 4097 * 4
-    assert ws(8192, 7168, 256) == 4 * 256 * 8192 * 3
+    assert ws(4096, 7168, 256) == 4 * 256 * 4096 * 4
+    assert ws(4097, 7168, 256) == 4 * 256 * 4097 * 3
+    assert ws(8192, 7168, 256) == 4 * 256 * 8192 * 2
 
 
 def test_binding_has_no_cpu_fallback():

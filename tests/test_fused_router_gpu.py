@@ -112,6 +112,7 @@ def test_fused_router_one_lane_holds_most_picks(G, TG):
                      "step) faulted the GPU on this case; the variant was removed and the case "
                      "stays off the GPU until that fault's cause is shown"))),
     (130, 2048, 8, 4, 8, "sigmoid", "top2sum", True, True, 2.0),    # saturating cap
+    (400, 7168, 8, 4, 8, "sigmoid", "top2sum", True, True, 0.0),    # 19 splits, a block per row
     (3000, 640, 8, 4, 8, "sigmoid", "top2sum", True, True, 0.0),    # 64-row tiles, ragged
     (2100, 1024, 1, 1, 2, "softmax", "max", False, False, 30.0),    # 64-row tiles, capped
 ])
@@ -146,7 +147,7 @@ def test_fused_router_split_path_full_width_sampled(M, splits):
     tokens, 2 of 56 at 8192 (the full workload)."""
     wl = WORKLOADS["fused_router_h7168"]
     assert mr.route_fused_router_workspace_size(M, wl.hidden_dim, wl.E) == \
-        4 * 256 * M * (splits + 1)
+        4 * 256 * M * splits
     hidden, w = make_router_inputs(wl, M)
     b = make_bias(wl)
     log(f"[gpu] route_fused_router split path M={M} H={wl.hidden_dim} ({splits} splits)")
@@ -158,17 +159,22 @@ def test_fused_router_split_path_full_width_sampled(M, splits):
     _check(hidden, w, b, wt, ids, rows, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
 
 
-def test_fused_router_split_path_deterministic_and_reused_workspace():
+@pytest.mark.parametrize("M,M2,H", [
+    (200, 50, 1024),    # 16 splits: a block per row sums them
+    (3000, 1000, 640),  # 5 splits each (64- and 32-row tiles): a wave per 8 rows
+])
+def test_fused_router_split_path_deterministic_and_reused_workspace(M, M2, H):
     """Two calls through one caller-owned workspace, the second smaller:
     bit-identical to fresh calls (the sums run in a fixed order)."""
     rng = np.random.default_rng(13)
-    hidden, w, b = _inputs(rng, 200, 1024)
-    ws = torch.empty(mr.route_fused_router_workspace_size(200, 1024, 256), dtype=torch.uint8,
+    hidden, w, b = _inputs(rng, M, H)
+    ws = torch.empty(mr.route_fused_router_workspace_size(M, H, 256), dtype=torch.uint8,
                      device="cuda")
+    log(f"[gpu] route_fused_router split path reused workspace M={M} then {M2}, H={H}")
     a = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
-    c = _run(hidden[:50], w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    c = _run(hidden[:M2], w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
     a2 = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum")
-    c2 = _run(hidden[:50], w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    c2 = _run(hidden[:M2], w, b, 8, 8, 4, True, "sigmoid", "top2sum")
     assert np.array_equal(a[0], a2[0]) and np.array_equal(a[1], a2[1])
     assert np.array_equal(c[0], c2[0]) and np.array_equal(c[1], c2[1])
 
