@@ -159,6 +159,24 @@ def test_fused_router_split_path_full_width_sampled(M, splits):
     _check(hidden, w, b, wt, ids, rows, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
 
 
+@pytest.mark.parametrize("M,H,G,TG,workspace", [
+    (130, 512, 8, 4, False),   # one kernel
+    (300, 1024, 8, 4, None),   # split path, 16 splits: a block per row
+    (77, 1024, 1, 1, None),    # split path, ungrouped
+    (3000, 640, 8, 4, None),   # split path, 5 splits: a wave per 8 rows
+])
+def test_fused_router_wide_bias(M, H, G, TG, workspace):
+    """A bias spread wider than 4 takes the exact-comparison selection in the
+    routing epilogue of every path."""
+    rng = np.random.default_rng(M + H)
+    hidden, w, _ = _inputs(rng, M, H, bias=False)
+    b = rng.uniform(-3.0, 3.0, 256).astype(np.float32)
+    log(f"[gpu] route_fused_router wide bias M={M} H={H} G={G} TG={TG} "
+        f"{'one kernel' if workspace is False else 'default'}")
+    wt, ids = _run(hidden, w, b, 8, G, TG, True, "sigmoid", "top2sum", workspace=workspace)
+    _check(hidden, w, b, wt, ids, np.arange(M), 8, G, TG, True, "sigmoid", "top2sum")
+
+
 @pytest.mark.parametrize("M,M2,H", [
     (200, 50, 1024),    # 16 splits: a block per row sums them
     (3000, 1000, 640),  # 5 splits each (64- and 32-row tiles): a wave per 8 rows

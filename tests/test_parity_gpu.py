@@ -80,6 +80,31 @@ def test_random_shapes(entry, E, G, TG, K, dtype, scoring, renorm, M, seed):
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("E,G,TG,K,dtype,M,half", [
+    (256, 8, 4, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, top-2-sum groups
+    (256, 1, 1, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, ungrouped
+    (160, 8, 3, 6, "f32", 777, 3.0),     # 160 experts in groups of 20
+    (384, 8, 4, 8, "bf16", 300, 3.0),    # generic kernel
+    (256, 8, 4, 8, "bf16", 1000, 1.2),   # widest window that keeps the keys (R = 4)
+])
+def test_wide_bias_takes_the_exact_path(E, G, TG, K, dtype, M, half):
+    """A selection-score spread wider than 4 (bias U(-3, 3)) makes the
+    fixed-point keys too coarse; the kernels then select on exact fp32
+    comparisons.  With U(-1.2, 1.2) the spread is about 3.4: keys on the
+    coarsest window, a step of 4 * 2^-23."""
+    rng = np.random.default_rng(E * 1000 + M)
+    x = random_logits(rng, M, E, dtype, std=1.5)
+    b = rng.uniform(-half, half, E).astype(np.float32)
+    assert (b.max() - b.min() > 4.0) == (half > 2.0)
+    log(f"[gpu] route_biased_grouped_topk wide bias E={E} G={G} TG={TG} K={K} {dtype} M={M} "
+        f"U(-{half}, {half})")
+    w, ids = route_gpu("route_biased_grouped_topk", to_device(x), K=K, G=G, TG=TG,
+                       scoring="sigmoid", bias=to_device(b), renorm=True)
+    sc, rule = oracle_args("route_biased_grouped_topk", "sigmoid")
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=G, TG=TG, rule=rule, K=K, renorm=True)
+    assert rep.ok(), rep.summary()
+
+
 @pytest.mark.parametrize("entry,scoring", [("route_biased_grouped_topk", "sigmoid"),
                                            ("route_grouped_topk", "softmax"),
                                            ("route_topk_softmax", "softmax")])
