@@ -36,6 +36,7 @@ def _compare(ids_np, E, w_np=None, workspace=None):
     (4096, 8, 256, 0, 256, 4),   # whole 512-assignment chunks
     (513, 1, 1024, -5, 1024, 5), # widest expert id (11 bits)
     (20000, 2, 1, -1, 1, 6),     # one expert, half the ids dropped
+    (70001, 8, 256, -2, 258, 7), # 274 blocks: the scan reads its columns in two batches
 ])
 def test_dispatch_random_ids(M, K, E, lo, hi, seed):
     rng = np.random.default_rng(seed)
