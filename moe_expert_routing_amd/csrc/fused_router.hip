@@ -558,7 +558,8 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     } else {
         kp = key_params(0.0f, 1.0f);
     }
-    // the logit of expert e, recomputed in the same order (rare paths only)
+    // the logit of expert e, summed in the same order (route_rows reads it only
+    // with one lane per row, so not here; it stays exact for any later use)
     const float* rsrc = part + rrow * kFrE;
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
         x, sub, rw, row < M, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
