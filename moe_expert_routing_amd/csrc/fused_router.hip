@@ -362,69 +362,77 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_partial_kernel(
         }
 }
 
-// Splits of exactly one hidden step (32-row tiles; 64 tokens or fewer of a
-// 7168-wide router): no ring, so no copies run ahead past the step.  The four
-// MFMA waves each copy one 8-row block of the hidden-state tile and their
-// eight W blocks into the same LDS layout as a ring stage, wait for them, and
-// do the step's MFMAs.
+// Splits of at most kFrNoRingSteps hidden steps on 32-row tiles (few
+// tokens): no ring, so no copies run past the split.  The four MFMA waves
+// each copy one 8-row block of the hidden-state tile and their eight W blocks
+// of every step of the split into the same LDS layout as a ring stage, wait
+// for all of them, and do the MFMAs step by step.
+constexpr int kFrNoRingSteps = 4;
 constexpr int kFrStepThreads = 64 * kFrMathWaves;
+static_assert(kFrNoRingSteps * (kFrABytes + kFrWBytes) <= 160 * 1024, "LDS of one workgroup");
 __global__ __launch_bounds__(kFrStepThreads) void fused_router_step_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w, int64_t M, int H,
-    float* __restrict__ part) {
-    __shared__ __align__(1024) unsigned char sA[kFrABytes];
-    __shared__ __align__(1024) unsigned char sW[kFrWBytes];
+    int nsplit, float* __restrict__ part) {
+    __shared__ __align__(1024) unsigned char sA[kFrNoRingSteps][kFrABytes];
+    __shared__ __align__(1024) unsigned char sW[kFrNoRingSteps][kFrWBytes];
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
-    const int step = blockIdx.y;
+    const int split = blockIdx.y, steps_all = H / kFrBK;
+    const int s_lo = split * steps_all / nsplit;
+    const int steps = (split + 1) * steps_all / nsplit - s_lo;  // 1 .. kFrNoRingSteps
     static_assert(kFrABytes / 1024 == kFrMathWaves, "one hidden-state block per MFMA wave");
-    {
-        const int m = 8 * wv + lane / 8;
-        lds_copy16(hidden + min(m0 + m, M - 1) * H + (int64_t)step * kFrBK + 8 * a_swz(m, lane % 8),
-                   lds_addr(sA + 1024 * wv));
-    }
-    const uint16_t* wk = w + (int64_t)step * kFrBK * kFrE;
+    const int m = 8 * wv + lane / 8;
+    const uint16_t* a_src = hidden + min(m0 + m, M - 1) * H + (int64_t)s_lo * kFrBK +
+                            8 * a_swz(m, lane % 8);
+    for (int q = 0; q < steps; ++q) {
+        lds_copy16(a_src + q * kFrBK, lds_addr(sA[q] + 1024 * wv));
+        const uint16_t* wk = w + (int64_t)(s_lo + q) * kFrBK * kFrE;
 #pragma unroll
-    for (int j = 0; j < kFrWCopies; ++j) {
-        const int k = 2 * (kFrWCopies * wv + j) + lane / 32;
-        lds_copy16(wk, 2u * (k * kFrE + 8 * w_swz(k, lane % 32)),
-                   lds_addr(sW + 1024 * (kFrWCopies * wv + j)));
+        for (int j = 0; j < kFrWCopies; ++j) {
+            const int k = 2 * (kFrWCopies * wv + j) + lane / 32;
+            lds_copy16(wk, 2u * (k * kFrE + 8 * w_swz(k, lane % 32)),
+                       lds_addr(sW[q] + 1024 * (kFrWCopies * wv + j)));
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // fragments and MFMAs of the step, as in fr_project
+    // fragments and MFMAs of each step, as in fr_project
     const int fa_m = lane % 32;
     const int g = lane / 16, gi = lane % 16;
-    bf16x8 af[kFrBK / 16], bfr[kFrBK / 16][2];
-#pragma unroll
-    for (int kk = 0; kk < kFrBK / 16; ++kk) {
-        af[kk] = *reinterpret_cast<const bf16x8*>(sA + fa_m * 128 +
-                                                  16 * a_swz(fa_m, 2 * kk + lane / 32));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int e = wv * 64 + nt * 32 + 16 * (g % 2) + 4 * (gi % 4);
-            i16x4 p[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = 16 * kk + 8 * (g / 2) + 4 * h + gi / 4;
-                p[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(sW + k * 512 + 16 * w_swz(k, e / 8) + 2 * (e % 8)));
-            }
-            bfr[kk][nt] = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    }
     f32x16 acc[2];
 #pragma unroll
     for (int q = 0; q < 16; ++q) { acc[0][q] = 0.f; acc[1][q] = 0.f; }
+    for (int q = 0; q < steps; ++q) {
+        bf16x8 af[kFrBK / 16], bfr[kFrBK / 16][2];
 #pragma unroll
-    for (int kk = 0; kk < kFrBK / 16; ++kk)
+        for (int kk = 0; kk < kFrBK / 16; ++kk) {
+            af[kk] = *reinterpret_cast<const bf16x8*>(sA[q] + fa_m * 128 +
+                                                      16 * a_swz(fa_m, 2 * kk + lane / 32));
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk][nt], acc[nt], 0, 0, 0);
+            for (int nt = 0; nt < 2; ++nt) {
+                const int e = wv * 64 + nt * 32 + 16 * (g % 2) + 4 * (gi % 4);
+                i16x4 p[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 16 * kk + 8 * (g / 2) + 4 * h + gi / 4;
+                    p[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(sW[q] + k * 512 + 16 * w_swz(k, e / 8) + 2 * (e % 8)));
+                }
+                bfr[kk][nt] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < kFrBK / 16; ++kk)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[nt] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk][nt], acc[nt], 0, 0, 0);
+    }
 
-    float* out = part + (int64_t)step * M * kFrE;
+    float* out = part + (int64_t)split * M * kFrE;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         const int n = wv * 64 + nt * 32 + (lane % 32);
@@ -614,10 +622,10 @@ route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
         hipLaunchKernelGGL(fused_router_partial_kernel<64>, dim3((unsigned)tiles, (unsigned)nsplit),
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
                            static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
-    else if (nsplit == f.H / kFrBK)  // every split one hidden step
+    else if ((f.H / kFrBK + nsplit - 1) / nsplit <= kFrNoRingSteps)  // a few steps per split
         hipLaunchKernelGGL(fused_router_step_kernel, dim3((unsigned)tiles, (unsigned)nsplit),
                            dim3(kFrStepThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
-                           static_cast<const uint16_t*>(f.w), f.M, f.H, part);
+                           static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
     else
         hipLaunchKernelGGL(fused_router_partial_kernel<32>, dim3((unsigned)tiles, (unsigned)nsplit),
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
@@ -666,7 +674,12 @@ SplitPlan fused_router_split_plan(int64_t M, int H) {
     if (M <= 0 || steps < 2) return {kFrRows, 1};
     const int64_t most = std::min<int64_t>(steps, 256 / tiles);
     if (most < 2) return {kFrRows, 1};
-    const int per_split = (steps + (int)most - 1) / (int)most;
+    int per_split = (steps + (int)most - 1) / (int)most;
+    // Each split also writes and re-reads 1 KiB of partial logits per token.
+    // Above 8 tokens a 32-row split takes at least 4 steps (measured: 64
+    // tokens of a 7168-wide router, 9.6 us a call against 11.9 with one step
+    // per split; at one token one step is best).
+    if (rows == 32 && M > 8) per_split = std::max(per_split, std::min(kFrNoRingSteps, steps));
     return {rows, (steps + per_split - 1) / per_split};
 }
 

@@ -154,11 +154,16 @@ def test_fused_router_workspace_size():
     assert ws(65536, 7168, 256) == 0
     # fp32 partials of every split, [M][256] each.
     # Up to 2048 tokens, tiles of 32 rows.  One tile and 112 steps of 64:
-    # 112 splits of one step.
+    # 112 splits of one step for up to 8 tokens, then at least 4 steps per
+    # split (28 splits).
     assert ws(1, 7168, 256) == 4 * 256 * 1 * 112
-    assert ws(32, 7168, 256) == 4 * 256 * 32 * 112
-    # 3 tiles: 56 splits of two steps (168 workgroups, one round)
-    assert ws(65, 7168, 256) == 4 * 256 * 65 * 56
+    assert ws(8, 7168, 256) == 4 * 256 * 8 * 112
+    assert ws(9, 7168, 256) == 4 * 256 * 9 * 28
+    assert ws(32, 7168, 256) == 4 * 256 * 32 * 28
+    # 3 tiles: 28 splits of four steps (84 workgroups)
+    assert ws(65, 7168, 256) == 4 * 256 * 65 * 28
+    # 16 tiles: 16 splits of seven steps (one round of 256 workgroups)
+    assert ws(512, 7168, 256) == 4 * 256 * 512 * 16
     # above 2048 tokens, tiles of 64 rows: 43 tiles -> 5 splits of 23 steps
     assert ws(2720, 7168, 256) == 4 * 256 * 2720 * 5
     # 64 tiles: 4 splits of 28 steps; 65 tiles: 3 of 38; 128 tiles: 2 of 56
