@@ -319,9 +319,9 @@ __device__ __forceinline__ void route_lanes16(float x, int j, bool store,
 // whole launch.  A operands come straight from global memory: in the MFMA
 // layout, lane (token i, quarter q) of fragment f holds hidden units
 // 32 f + 8 q .. +7 of token i, one 16-byte load.  A wave loads its
-// fragments 4 at a time into two register buffers, the next batch (or the
-// next tile's first) in flight while the current one is multiplied and while
-// a finished tile is reduced.  Partial tiles of the 8 waves are added in LDS
+// fragments 4 at a time into two register buffers, both in flight: the next
+// two batches (or the next tile's first two) load while the current one is
+// multiplied and while a finished tile is reduced.  Partial tiles of the 8 waves are added in LDS
 // in wave order, then soft-capped and routed by 16 lanes per token.
 constexpr int kSmWaves = 8;
 constexpr int kSmThreads = kSmWaves * kWave;
@@ -427,21 +427,25 @@ __global__ __launch_bounds__(kSmThreads) void small_router_mfma_kernel(
         }
     };
 
-    // Two batch buffers: batch b + 1 loads while batch b is multiplied, and
-    // the next tile's first batch is in flight while this tile is reduced.
+    // Two batch buffers, both in flight: batch b sits in P[b % 2]; once it
+    // is multiplied its buffer takes batch b + 2, so batches b + 1 and b + 2
+    // load during the MFMAs of batch b, and the next tile's first two
+    // batches load while this tile is reduced.
     Batch P[2];
     int64_t g = blockIdx.x;
     load(g, 0, P[0]);
+    if (NB > 1) load(g, 1, P[1]);
     for (; g < tiles; g += gridDim.x) {
         const int64_t gn = g + gridDim.x < tiles ? g + gridDim.x : g;
 #pragma unroll
         for (int r = 0; r < 4; ++r) { c0[r] = 0.f; c1[r] = 0.f; }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            if (b + 1 < NB) load(g, b + 1, P[(b + 1) % 2]);
             compute(P[b % 2], b);
+            if (b + 2 < NB) load(g, b + 2, P[b % 2]);
         }
         load(gn, 0, P[0]);
+        if (NB > 1) load(gn, 1, P[1]);
 
         // D layout: lane (expert i16, quarter q) holds tokens 4q .. 4q+3
 #pragma unroll
