@@ -366,38 +366,6 @@ __global__ __launch_bounds__(kSmThreads) void small_router_mfma_kernel(
     constexpr int FM = NB * kSmBatch;  // fragment slots per wave
     static_assert(FM <= kSmFragMax, "fragments per wave");
     bf16x8 wf[FM];
-    {
-        uint4 raw[FM];
-        const int row = lane / 2, half = lane % 2;  // this lane's 16 bytes of an image
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int k = 32 * (wv + kSmWaves * i) + row;
-            const bool ok = i < fw && k < H && (E == 16 || half == 0);
-            raw[i] = *reinterpret_cast<const uint4*>(w + (ok ? (int64_t)k * E + 8 * half : 0));
-            if (!ok) raw[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-        unsigned char* img = wstage[wv];
-#pragma unroll
-        for (int rr = 0; rr < NB; ++rr) {
-#pragma unroll
-            for (int i = 0; i < kSmBatch; ++i)
-                *reinterpret_cast<uint4*>(img + 1024 * i + 16 * lane) = raw[kSmBatch * rr + i];
-            wave_lds_sync();
-#pragma unroll
-            for (int i = 0; i < kSmBatch; ++i) {
-                i16x4 h2[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int off = 1024 * i + 32 * (8 * q + 4 * h + i16 / 4) + 8 * (i16 % 4);
-                    h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(img + off));
-                }
-                wf[kSmBatch * rr + i] = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-            wave_lds_sync();
-        }
-    }
-
     struct Batch {
         uint4 a[kSmBatch];
     };
@@ -433,8 +401,41 @@ __global__ __launch_bounds__(kSmThreads) void small_router_mfma_kernel(
     // batches load while this tile is reduced.
     Batch P[2];
     int64_t g = blockIdx.x;
+    // the first tile's hidden states load while W is turned into B operands
     load(g, 0, P[0]);
     if (NB > 1) load(g, 1, P[1]);
+    {
+        uint4 raw[FM];
+        const int row = lane / 2, half = lane % 2;  // this lane's 16 bytes of an image
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int k = 32 * (wv + kSmWaves * i) + row;
+            const bool ok = i < fw && k < H && (E == 16 || half == 0);
+            raw[i] = *reinterpret_cast<const uint4*>(w + (ok ? (int64_t)k * E + 8 * half : 0));
+            if (!ok) raw[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        unsigned char* img = wstage[wv];
+#pragma unroll
+        for (int rr = 0; rr < NB; ++rr) {
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i)
+                *reinterpret_cast<uint4*>(img + 1024 * i + 16 * lane) = raw[kSmBatch * rr + i];
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i) {
+                i16x4 h2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int off = 1024 * i + 32 * (8 * q + 4 * h + i16 / 4) + 8 * (i16 % 4);
+                    h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(img + off));
+                }
+                wf[kSmBatch * rr + i] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            wave_lds_sync();
+        }
+    }
+
     for (; g < tiles; g += gridDim.x) {
         const int64_t gn = g + gridDim.x < tiles ? g + gridDim.x : g;
 #pragma unroll
