@@ -13,8 +13,9 @@
 //   1. hist:  each block counts its chunk per expert (LDS atomics) into its
 //             row cnt[b][*];
 //   2. scan:  64 experts per block, each column cnt[*][e] split over 16
-//             segments, turns each column into exclusive offsets across
-//             blocks and writes the expert's total;
+//             segments (held in registers between its two passes), turns
+//             each column into exclusive offsets across blocks and writes
+//             the expert's total;
 //   3. place: each block scans the totals into expert offsets (block 0 also
 //             writes counts and offsets), recounts its chunk per wave, so that every wave
 //             starts from its own cursor per expert (the expert offset plus
@@ -75,14 +76,25 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     const bool active = e < E;
     const int per = (B + S - 1) / S;
     const int b0 = min(seg * per, B), b1 = min(b0 + per, B);
+    // up to S * kScanBatch blocks a segment stays in registers between the
+    // two passes; beyond, the second pass reads it again
+    const bool held = per <= kScanBatch;
+    int v[kScanBatch];
     int part = 0;
-    for (int b = b0; b < b1; b += kScanBatch) {
-        int v[kScanBatch];
+    if (held) {
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i)
-            v[i] = (active && b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+            v[i] = (active && b0 + i < b1) ? cnt[(int64_t)(b0 + i) * E + e] : 0;
 #pragma unroll
         for (int i = 0; i < kScanBatch; ++i) part += v[i];
+    } else {
+        for (int b = b0; b < b1; b += kScanBatch) {
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i)
+                v[i] = (active && b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) part += v[i];
+        }
     }
     s_part[seg][lane] = part;
     __syncthreads();
@@ -93,15 +105,22 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
         total += v;
     }
     if (active) {
-        for (int b = b0; b < b1; b += kScanBatch) {
-            int v[kScanBatch];
-#pragma unroll
-            for (int i = 0; i < kScanBatch; ++i)
-                v[i] = (b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+        if (held) {
 #pragma unroll
             for (int i = 0; i < kScanBatch; ++i) {
-                if (b + i < b1) cnt[(int64_t)(b + i) * E + e] = start;
+                if (b0 + i < b1) cnt[(int64_t)(b0 + i) * E + e] = start;
                 start += v[i];
+            }
+        } else {
+            for (int b = b0; b < b1; b += kScanBatch) {
+#pragma unroll
+                for (int i = 0; i < kScanBatch; ++i)
+                    v[i] = (b + i < b1) ? cnt[(int64_t)(b + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < kScanBatch; ++i) {
+                    if (b + i < b1) cnt[(int64_t)(b + i) * E + e] = start;
+                    start += v[i];
+                }
             }
         }
         if (seg == 0) totals[e] = total;
