@@ -14,7 +14,9 @@ from workloads import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_bias
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,K,rsf", [(4096, 9, 2.5), (77, 9, None), (1, 2, 1.0), (1000, 13, 0.3)])
+@pytest.mark.parametrize("M,K,rsf", [(4096, 9, 2.5), (77, 9, None), (1, 2, 1.0), (1000, 13, 0.3),
+                                     (300, 4, 2.5), (1000, 8, 1.0), (200, 20, 2.5), (65, 33, None),
+                                     (40, 64, 0.5)])  # every row width: 2 .. 64 lanes
 def test_fuse_shared_expert(M, K, rsf):
     wl = WORKLOADS["biased_grouped_e256"]
     x, b = make_logits(wl, M), make_bias(wl)
@@ -31,7 +33,8 @@ def test_fuse_shared_expert(M, K, rsf):
 
 
 @pytest.mark.parametrize("M,K,hi", [(5000, 8, 256), (333, 2, 4), (1000, 13, 30), (64, 16, 10),
-                                    (100, 17, 50), (257, 40, 30), (31, 64, 1000)])
+                                    (100, 17, 50), (257, 40, 30), (31, 64, 1000), (700, 3, 5),
+                                    (99, 4, 3)])
 def test_sort_ids(M, K, hi):
     rng = np.random.default_rng(K)
     i0 = rng.integers(0, hi, size=(M, K)).astype(np.int32)   # repeats: stable by slot
