@@ -159,6 +159,29 @@ def test_fused_router_split_path_full_width_sampled(M, splits):
     _check(hidden, w, b, wt, ids, rows, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
 
 
+# every epilogue instantiation (scoring, bias, group rule) on every path:
+# the single kernel, the split path reduced a block per row (8 splits) and
+# a wave per 8 rows (4 splits)
+_COMBOS = [("softmax", False, 1, "max"), ("sigmoid", True, 1, "top2sum"), ("sigmoid", False, 1, "max"),
+           ("sigmoid", True, 8, "top2sum"), ("sigmoid", False, 8, "top2sum"),
+           ("softmax", False, 8, "max"), ("sigmoid", True, 8, "max"), ("sigmoid", False, 8, "max")]
+_PATHS = [(96, 256, False), (130, 2048, None), (77, 1024, None)]
+
+
+@pytest.mark.parametrize("scoring,bias,G,rule", _COMBOS)
+@pytest.mark.parametrize("M,H,workspace", _PATHS)
+def test_fused_router_every_epilogue(M, H, workspace, scoring, bias, G, rule):
+    """Each (scoring, bias, group rule) instantiation of the routing epilogue
+    on the single kernel and on both split-path reductions."""
+    rng = np.random.default_rng(M * 31 + G * 7 + len(rule) + (3 if bias else 0))
+    hidden, w, b = _inputs(rng, M, H, bias=bias)
+    TG = 3 if G == 8 else 1
+    log(f"[gpu] route_fused_router epilogue {scoring} bias={bias} G={G} {rule} M={M} H={H} "
+        f"{'one kernel' if workspace is False else 'split'}")
+    wt, ids = _run(hidden, w, b, 6, G, TG, True, scoring, rule, workspace=workspace)
+    _check(hidden, w, b, wt, ids, np.arange(M), 6, G, TG, True, scoring, rule)
+
+
 @pytest.mark.parametrize("M,H,G,TG,workspace", [
     (130, 512, 8, 4, False),   # one kernel
     (130, 2048, 8, 4, None),   # split path, 8 splits: a block per row
