@@ -80,6 +80,39 @@ def test_random_shapes(entry, E, G, TG, K, dtype, scoring, renorm, M, seed):
     assert rep.ok(), rep.summary()
 
 
+def _kernel_variants():
+    """(entry, dtype, E, G, TG, K, scoring, with_bias): every specialised
+    routing kernel the entry points reach (bf16 and fp32 at 256 experts,
+    fp32 at 160 and at 8)."""
+    out = []
+    for dtype, E in (("bf16", 256), ("f32", 256), ("f32", 160)):
+        out += [("route_topk_softmax", dtype, E, 1, 1, 8, "softmax", False),
+                ("route_biased_grouped_topk", dtype, E, 1, 1, 8, "sigmoid", True),
+                ("route_biased_grouped_topk", dtype, E, 1, 1, 8, "sigmoid", False),
+                ("route_biased_grouped_topk", dtype, E, 8, 4, 8, "sigmoid", True),
+                ("route_biased_grouped_topk", dtype, E, 8, 4, 8, "sigmoid", False),
+                ("route_grouped_topk", dtype, E, 8, 3, 6, "softmax", False),
+                ("route_grouped_topk", dtype, E, 8, 3, 6, "sigmoid", False)]
+    out += [("route_topk_softmax", "f32", 8, 1, 1, 2, "softmax", False),
+            ("route_biased_grouped_topk", "f32", 8, 1, 1, 2, "sigmoid", True),
+            ("route_grouped_topk", "f32", 8, 1, 1, 1, "sigmoid", False)]
+    return out
+
+
+@pytest.mark.parametrize("entry,dtype,E,G,TG,K,scoring,with_bias", _kernel_variants())
+def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias):
+    rng = np.random.default_rng(E * 100 + G * 10 + K + (1 if with_bias else 0) + len(scoring))
+    M = 1000  # ragged last tile for every layout
+    x = random_logits(rng, M, E, dtype, std=1.5)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
+    log(f"[gpu] {entry} {dtype} E={E} G={G} TG={TG} K={K} {scoring} bias={with_bias}")
+    w, ids = route_gpu(entry, to_device(x), K=K, G=G, TG=TG, scoring=scoring,
+                       bias=None if b is None else to_device(b), renorm=True)
+    sc, rule = oracle_args(entry, scoring)
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=G, TG=TG, rule=rule, K=K, renorm=True)
+    assert rep.ok(), rep.summary()
+
+
 @pytest.mark.parametrize("E,G,TG,K,dtype,M,half", [
     (256, 8, 4, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, top-2-sum groups
     (256, 1, 1, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, ungrouped
