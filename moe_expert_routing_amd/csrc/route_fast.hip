@@ -42,6 +42,9 @@ route_status_t launch_route_generic(const RouteProblem& p);
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unbounded
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Raw logits of one lane (kept packed until scoring so that the next tile's
 // loads can be in flight while this tile is scored).
@@ -115,22 +118,27 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
         const int64_t row = min(t * RPW + rw, M - 1);
         r.load(logits + row * E + sub * VPL);
     };
+    // The bias (one float4 per lane) is requested before the first tile, so
+    // that the prologue below needs only the bias to have arrived.
+    static_assert(!BIAS || E <= 4 * kWave, "one float4 of bias per lane");
+    const bool has_b = BIAS && 4 * lane < E;
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_b) bq = *reinterpret_cast<const float4*>(bias + 4 * lane);
     RawLane<T, VPL> ra, rb;  // ping-pong: one tile routed while the next loads
-    if (tile < tiles) load_tile(ra, tile);  // in flight during the prologue below
+    // In flight during the prologue below.  A wave without a tile loads the
+    // last one anyway: with the load unconditional, the prologue's wait
+    // counts the bias alone.
+    load_tile(ra, tile < tiles ? tile : tiles - 1);
 
     // ---- key window.  Keys are compared only within a row; the window holds
     // every selection score c = s + bias of any row, so it comes from the
     // range of the bias, reduced over the wave.
     KeyParams kp;
     if constexpr (BIAS) {
-        float bmin = INFINITY, bmax = -INFINITY;
-        for (int e = 4 * lane; e < E; e += 4 * kWave) {
-            const float4 d = *reinterpret_cast<const float4*>(bias + e);
-            bmin = fminf(fminf(bmin, d.x), fminf(d.y, fminf(d.z, d.w)));
-            bmax = fmaxf(fmaxf(bmax, d.x), fmaxf(d.y, fmaxf(d.z, d.w)));
-        }
+        const float bmin = has_b ? fminf(fminf(bq.x, bq.y), fminf(bq.z, bq.w)) : INFINITY;
+        const float bmax = has_b ? fmaxf(fmaxf(bq.x, bq.y), fmaxf(bq.z, bq.w)) : -INFINITY;
+        if (wv == 0 && has_b) *reinterpret_cast<float4*>(s_bias + bias_chunk<E>(lane) * 4) = bq;
         kp = key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
-        for (int e = threadIdx.x; e < E; e += kWavesPerBlock * kWave) s_bias[bias_elem<E>(e)] = bias[e];
         __syncthreads();
     } else {
         kp = key_params(0.0f, 1.0f);
@@ -146,6 +154,10 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
             x, sub, rw, valid, row, my_row, s_bias, kp, TG, K, renorm, w_out, id_out,
             [&](int e) { return load_one<T>(xr, e); });
     };
+    // The second tile is requested only once the first has arrived: at the
+    // start every wave of the grid requests at once, and second tiles
+    // requested alongside the first ones delay them.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     while (tile < tiles) {
         if (tile + tstride < tiles) load_tile(rb, tile + tstride);
         route_tile(ra, tile);

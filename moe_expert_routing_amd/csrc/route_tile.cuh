@@ -13,6 +13,7 @@ constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppXor3 = 0x1B;     // quad_perm [3,2,1,0]
 constexpr int kDppMirror8 = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
+constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <-> 15 - i within 16
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -69,16 +70,20 @@ __device__ __forceinline__ void row_argmax(float& v, int& i) {
 #undef MOE_ROUTE_ARGMAX_STEP
 }
 
-// Whole-wave min / max (all lanes hold the result).
+// Whole-wave min / max (all lanes hold the result), on the VALU: DPP within
+// each row of 16 lanes, then the four row results through SGPRs.
+__device__ __forceinline__ float lane_f32(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_min_all(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fminf(v, shfl_xor(v, o));
-    return v;
+    v = row_min<8>(v);
+    v = fminf(v, dpp_f32<kDppRowMirror>(v));
+    return fminf(fminf(lane_f32(v, 0), lane_f32(v, 16)), fminf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ float wave_max_all(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-    return v;
+    v = row_max<8>(v);
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 
 template <typename T>
