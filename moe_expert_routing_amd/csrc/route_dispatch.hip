@@ -33,10 +33,10 @@
 namespace moe_route {
 namespace {
 
-constexpr int kDispWaves = 4;
+constexpr int kDispWaves = 8;                            // 2 per SIMD: shorter place loops
 constexpr int kDispThreads = kDispWaves * kWave;
-constexpr int kPerLane = 8;                              // assignments per lane
-constexpr int kWaveChunk = kPerLane * kWave;             // 512 per wave
+constexpr int kPerLane = 4;                              // assignments per lane
+constexpr int kWaveChunk = kPerLane * kWave;             // 256 per wave
 constexpr int kBlockChunk = kDispWaves * kWaveChunk;     // 2048 per block
 constexpr int kScanThreads = 1024;                       // >= max experts
 constexpr int kScanBatch = 16;                           // loads in flight per thread
