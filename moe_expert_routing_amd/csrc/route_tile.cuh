@@ -332,8 +332,7 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
 #pragma unroll
             for (int s = 0; s < SLOTS; ++s) wk[s] = L[s];
         } else {
-#pragma unroll 1
-            for (int r = 0; r < K; ++r) {
+            auto round = [&](int r) {
                 const uint32_t w = row_max_u32<LPR>(L[0]);
                 w_last = w;
                 const bool mine = (L[0] == w);
@@ -344,6 +343,19 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
                     if (SLOTS == 1 || r < LPR) wk[0] = w;
                     else wk[SLOTS - 1] = w;
                 }
+            };
+            if constexpr (BIAS) {
+                // unrolled to KMAX rounds, leaving at the first round past K:
+                // ~2% faster for the biased kernels, whose register count it
+                // leaves alone (the others grow by ~13 VGPRs)
+#pragma unroll
+                for (int r = 0; r < KMAX; ++r) {
+                    if (r >= K) break;
+                    round(r);
+                }
+            } else {
+#pragma unroll 1
+                for (int r = 0; r < K; ++r) round(r);
             }
         }
     };
