@@ -113,6 +113,23 @@ def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias)
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("K", [1, 3, 5, 7])
+@pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
+def test_biased_kernel_every_k(K, G, TG):
+    """The biased kernels unroll their merge rounds to eight and leave after
+    the K-th: every K below eight, grouped and ungrouped."""
+    rng = np.random.default_rng(300 + 10 * K + G)
+    M = 777
+    x = random_logits(rng, M, 256, "bf16", std=1.5)
+    b = (rng.standard_normal(256) * 0.1).astype(np.float32)
+    log(f"[gpu] route_biased_grouped_topk bf16 E=256 G={G} TG={TG} K={K} M={M}")
+    w, ids = route_gpu("route_biased_grouped_topk", to_device(x), K=K, G=G, TG=TG,
+                       scoring="sigmoid", bias=to_device(b), renorm=True)
+    sc, rule = oracle_args("route_biased_grouped_topk", "sigmoid")
+    rep = compare(x, w, ids, scoring=sc, bias=b, G=G, TG=TG, rule=rule, K=K, renorm=True)
+    assert rep.ok(), rep.summary()
+
+
 @pytest.mark.parametrize("E,G,TG,K,dtype,M,half", [
     (256, 8, 4, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, top-2-sum groups
     (256, 1, 1, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, ungrouped
