@@ -63,6 +63,21 @@ def test_fused_router_small(M, H, G, TG, K, scoring, rule, bias, renorm, path):
     _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, renorm, scoring, rule)
 
 
+@pytest.mark.parametrize("K", [1, 5])
+@pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
+@pytest.mark.parametrize("path", ["one_kernel", "default"])
+def test_fused_router_biased_k_below_eight(K, G, TG, path):
+    """The biased epilogues unroll their merge rounds to eight and leave after
+    the K-th."""
+    M, H = 130, 512
+    rng = np.random.default_rng(700 + 10 * K + G)
+    hidden, w, b = _inputs(rng, M, H, bias=True)
+    log(f"[gpu] route_fused_router M={M} H={H} G={G} TG={TG} K={K} biased {path}")
+    wt, ids = _run(hidden, w, b, K, G, TG, True, "sigmoid", "top2sum",
+                   workspace=False if path == "one_kernel" else None)
+    _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, True, "sigmoid", "top2sum")
+
+
 @pytest.mark.parametrize("M,H,G,TG,K,scoring,rule,bias,renorm,cap", [
     (200, 256, 1, 1, 2, "softmax", "max", False, False, 30.0),   # top-2 softmax, cap 30
     (77, 512, 1, 1, 1, "softmax", "max", False, False, 5.0),     # top-1 softmax
