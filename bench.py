@@ -30,7 +30,7 @@ WORKLOAD = "biased_grouped_e256"
 # WRITE_SIZE runs scaled by a plain copy of known size; valid only for the
 # kernel sources they were taken on.
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "route_fast_biased_grouped_e256_m65536_traffic.txt")
-KERNEL_SOURCES = ("route_fast.hip", "route_tile.cuh", "route_common.cuh")
+KERNEL_SOURCES = ("route_fast.hip", "route_tile.hpp", "route_common.hpp")
 
 
 def kernel_source_digest():
@@ -77,8 +77,35 @@ def algorithmic_bytes(M, E, K, logit_bytes, bias=True):
     return M * E * logit_bytes + M * K * 8 + (E * 4 if bias else 0)
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The oracle as it stands, single-threaded, on the same workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    """Cores this process may run on, at most 16 (a one-GPU machine's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, budget_s=12.0, gpu_out=None):
+    """The oracle as it stands on the same workload, timed on the host: one
+    core, then the rows split over every core (one thread per core, each
+    calling the oracle on its rows; the oracle's C routine releases the GIL).
+    With gpu_out = (weights, ids) of the GPU on this batch, an untimed oracle
+    pass is also compared with it row by row, and the counts (exact rows,
+    near-tie rows by class, failures) are returned."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -86,22 +113,50 @@ def cpu_baseline(wl, budget_s=12.0):
 
     x = make_logits(wl)
     b = make_bias(wl)
-    rows = 0
+    M = x.shape[0]
+    args = dict(scoring=oracle.SIGMOID, bias=b, num_expert_group=wl.G, topk_group=wl.TG,
+                group_rule=oracle.GROUP_TOP2SUM, renormalize=wl.renormalize)
+
+    def run_rows(lo, hi):
+        return oracle.route(x[lo:hi], wl.K, **args)
+
+    # one core: full passes over the batch for half the budget
     t0 = time.perf_counter()
     reps = 0
     while True:
-        oracle.route(x, wl.K, scoring=oracle.SIGMOID, bias=b, num_expert_group=wl.G,
-                     topk_group=wl.TG, group_rule=oracle.GROUP_TOP2SUM,
-                     renormalize=wl.renormalize)
-        rows += x.shape[0]
+        run_rows(0, M)
         reps += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if time.perf_counter() - t0 >= budget_s / 2:
             break
-    dt = time.perf_counter() - t0
+    one = reps * M / (time.perf_counter() - t0)
+    # every core: the batch split into one row range per thread
+    n = host_cores()
+    bounds = [(M * i // n, M * (i + 1) // n) for i in range(n)]
+    t0 = time.perf_counter()
+    reps_all = 0
+    with ThreadPoolExecutor(n) as ex:
+        while True:
+            list(ex.map(lambda r: run_rows(*r), bounds))
+            reps_all += 1
+            if time.perf_counter() - t0 >= budget_s / 2:
+                break
+    dt_all = time.perf_counter() - t0
+    res = {"value": reps_all * M / dt_all, "unit": "tokens/s", "cores": n, "kind": "oracle",
+           "sample": f"{reps_all} full passes over the {M}-token batch split over {n} threads "
+                     f"({dt_all:.1f} s); one core: {reps} passes at {one:.0f} tokens/s "
+                     f"(C oracle in double precision)",
+           "one_core_value": one, "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    parity = None
+    if gpu_out is not None:
+        sys.path.insert(0, os.path.join(HERE, "tests"))
+        from parity_check import compare
+        rep = compare(x, gpu_out[0], gpu_out[1], scoring=oracle.SIGMOID, bias=b, G=wl.G,
+                      TG=wl.TG, rule=oracle.GROUP_TOP2SUM, K=wl.K, renorm=wl.renormalize)
+        parity = {"rows": rep.rows, "exact": rep.exact, "near_tie_k": rep.near_tie_k,
+                  "near_tie_order": rep.near_tie_order, "near_tie_group": rep.near_tie_group,
+                  "failures": len(rep.failures)}
     del np
-    return {"value": rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full passes over the {x.shape[0]}-token batch "
-                      f"({dt:.1f} s, single-threaded C oracle in double precision)"}
+    return res, parity
 
 
 def _events(n):
@@ -578,7 +633,8 @@ def main():
     if args.all_configs:
         measure_all(args.all_out)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(
+            wl, args.cpu_seconds, (ws[0].cpu().numpy(), ids[0].cpu().numpy()))
     print(json.dumps(result), flush=True)
 
 

@@ -24,7 +24,10 @@
  *           expert index first.  weights[r][k] belongs to ids[r][k].
  * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).  Work
  *           is only enqueued; nothing is synchronised, allocated or freed.
- * Threads.  Entry points are reentrant and keep no state between calls.
+ * Threads.  Entry points are reentrant.  The only state the library keeps is
+ *           a cache, filled on first use and safe under concurrent calls, of
+ *           each device's compute-unit count and of each kernel's resident
+ *           blocks per compute unit.
  * Errors.   Arguments are checked on the host before any HIP call:
  *             ROUTE_EINVAL   the arguments do not define a routing problem
  *                            (null pointer with num_tokens > 0, num_tokens < 0,
@@ -122,12 +125,16 @@ route_status_t route_grouped_topk(const void* gating_output, route_dtype_t dtype
  * emitted weight is the UNBIASED s of each chosen expert, optionally divided
  * by the sum of the K weights.  num_expert_group == topk_group == 1 is the
  * sigmoid-with-bias top-k the [AITER] page swaps in.
- *   correction_bias  [num_experts] float32, or NULL for all zeros.
+ *   correction_bias  [num_experts] of type bias_dtype, or NULL for all zeros.
+ *   bias_dtype       ROUTE_F32, or ROUTE_BF16: the [AITER] call ("Code
+ *                    analysis") casts the bias to the logits' dtype before
+ *                    passing it; bf16 entries are widened exactly to fp32.
+ *                    An unknown value is ROUTE_EINVAL (also with a NULL bias).
  *   With num_expert_group > 1 every group needs at least two experts.
  */
 route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_t dtype,
-                                         const float* correction_bias, int64_t num_tokens,
-                                         int32_t num_experts, int32_t top_k,
+                                         const void* correction_bias, route_dtype_t bias_dtype,
+                                         int64_t num_tokens, int32_t num_experts, int32_t top_k,
                                          int32_t num_expert_group, int32_t topk_group,
                                          int32_t renormalize, float* topk_weights,
                                          int32_t* topk_ids, void* stream);
@@ -140,7 +147,8 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  * num_expert_group / topk_group, top_k, renormalize).
  *   hidden_states  [num_tokens, hidden_dim] bf16
  *   router_weight  [hidden_dim, num_experts] bf16 (expert index contiguous)
- *   correction_bias [num_experts] float32 or NULL (zeros)
+ *   correction_bias [num_experts] of type bias_dtype (float32, or bf16 as in
+ *                  route_biased_grouped_topk) or NULL (zeros)
  *   logit_softcap  0, or a cap c: every logit l is replaced by c * tanh(l / c)
  *                  before scoring ([ROUTING] section 5, soft-capping); tanh
  *                  is increasing, so the cap changes weights, not choices.
@@ -160,7 +168,8 @@ route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_
  *   num_experts == 256: hidden_dim a positive multiple of 64 (MFMA router);
  *   num_experts 8 or 16 ([ROUTING] section 5's small-router case):
  *     hidden_dim a positive multiple of 8, num_expert_group == 1; no
- *     workspace is used (its size is 0).
+ *     workspace is used (its size is 0; a workspace passed anyway is
+ *     ignored).
  * Other valid shapes return ROUTE_ENOTSUP.  A misaligned workspace,
  * workspace_bytes without a workspace, or a workspace smaller than required
  * is ROUTE_EINVAL.
@@ -169,8 +178,9 @@ size_t route_fused_router_workspace_size(int64_t num_tokens, int32_t hidden_dim,
                                          int32_t num_experts);
 route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
                                   int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
-                                  route_scoring_t scoring_func, const float* correction_bias,
-                                  route_group_score_t group_score, int32_t top_k,
+                                  route_scoring_t scoring_func, const void* correction_bias,
+                                  route_dtype_t bias_dtype, route_group_score_t group_score,
+                                  int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, float logit_softcap, float* topk_weights,
                                   int32_t* topk_ids, void* workspace, size_t workspace_bytes,

@@ -54,8 +54,9 @@ def lib() -> ctypes.CDLL:
     p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.route_topk_softmax.argtypes = [p, i32, i64, i32, i32, i32, p, p, p]
     L.route_grouped_topk.argtypes = [p, i32, i64, i32, i32, i32, i32, i32, i32, p, p, p]
-    L.route_biased_grouped_topk.argtypes = [p, i32, p, i64, i32, i32, i32, i32, i32, p, p, p]
-    L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32,
+    L.route_biased_grouped_topk.argtypes = [p, i32, p, i32, i64, i32, i32, i32, i32, i32, p, p,
+                                            p]
+    L.route_fused_router.argtypes = [p, p, i64, i32, i32, i32, p, i32, i32, i32, i32, i32, i32,
                                      ctypes.c_float, p, p, p, ctypes.c_size_t, p]
     L.route_fused_router_workspace_size.argtypes = [i64, i32, i32]
     L.route_fused_router_workspace_size.restype = ctypes.c_size_t
@@ -93,6 +94,20 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return ROUTE_BF16
     raise ValueError(f"router logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _bias_code(bias, E) -> int:
+    """dtype code of a correction bias of shape [E] (float32, or bfloat16 as the
+    aiter-style call passes it in the logits' dtype); float32 for None."""
+    if bias is None:
+        return ROUTE_F32
+    if tuple(bias.shape) != (E,):
+        raise ValueError(f"correction_bias must have shape [{E}]")
+    if bias.dtype == torch.float32:
+        return ROUTE_F32
+    if bias.dtype == torch.bfloat16:
+        return ROUTE_BF16
+    raise ValueError(f"correction_bias must be float32 or bfloat16, got {bias.dtype}")
 
 
 def _ptr(t):
@@ -164,15 +179,15 @@ def route_grouped_topk(gating_output, top_k, num_expert_group, topk_group, renor
 def route_biased_grouped_topk(gating_output, correction_bias, top_k, num_expert_group=1,
                               topk_group=1, renormalize=False, topk_weights=None, topk_ids=None,
                               stream=None):
-    """Sigmoid + correction bias, top-2-sum group score; weights are unbiased."""
+    """Sigmoid + correction bias, top-2-sum group score; weights are unbiased.
+    correction_bias: None, or [E] float32 or bfloat16 (widened exactly)."""
     M, E = gating_output.shape
     w, ids = _outputs(M, top_k, gating_output.device, topk_weights, topk_ids)
-    if correction_bias is not None:
-        if correction_bias.dtype != torch.float32 or tuple(correction_bias.shape) != (E,):
-            raise ValueError("correction_bias must be float32 of shape [E]")
+    bias_code = _bias_code(correction_bias, E)
     _need_device(gating_output, correction_bias, w, ids)
     _check(lib().route_biased_grouped_topk(_ptr(gating_output), _dtype_code(gating_output),
-                                           _ptr(correction_bias), M, E, top_k, num_expert_group,
+                                           _ptr(correction_bias), bias_code, M, E, top_k,
+                                           num_expert_group,
                                            topk_group, int(bool(renormalize)), _ptr(w), _ptr(ids),
                                            _stream(gating_output.device, stream)),
            "route_biased_grouped_topk")
@@ -205,9 +220,7 @@ def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, 
     rules = {"max": ROUTE_GROUP_MAX, "top2sum": ROUTE_GROUP_TOP2_SUM}
     if group_score not in rules:
         raise ValueError(f"unknown group score {group_score!r}")
-    if correction_bias is not None:
-        if correction_bias.dtype != torch.float32 or tuple(correction_bias.shape) != (E,):
-            raise ValueError("correction_bias must be float32 of shape [E]")
+    bias_code = _bias_code(correction_bias, E)
     w, ids = _outputs(M, top_k, hidden_states.device, topk_weights, topk_ids)
     ws_ptr, ws_bytes = None, 0
     if workspace is None:
@@ -220,7 +233,8 @@ def route_fused_router(hidden_states, router_weight, top_k, num_expert_group=1, 
     _need_device(hidden_states, router_weight, correction_bias, w, ids)
     _check(lib().route_fused_router(_ptr(hidden_states), _ptr(router_weight), M, H, E,
                                     _scoring_code(scoring_func), _ptr(correction_bias),
-                                    rules[group_score], top_k, num_expert_group, topk_group,
+                                    bias_code, rules[group_score], top_k, num_expert_group,
+                                    topk_group,
                                     int(bool(renormalize)), float(logit_softcap), _ptr(w),
                                     _ptr(ids), ws_ptr, ws_bytes,
                                     _stream(hidden_states.device, stream)),

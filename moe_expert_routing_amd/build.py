@@ -11,6 +11,7 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -30,17 +31,23 @@ CFLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source (in parallel, one hipcc per source) and link."""
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
     with tempfile.TemporaryDirectory(prefix="moe_route_build_") as tmp:
-        objs = []
+        cmds, objs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            subprocess.check_call(cmd)
+            cmds.append([HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        if verbose:
+            for cmd in cmds:
+                print(" ".join(cmd), flush=True)
+        with ThreadPoolExecutor(jobs) as ex:
+            for rc, cmd in zip(ex.map(subprocess.call, cmds), cmds):
+                if rc != 0:
+                    raise subprocess.CalledProcessError(rc, cmd)
         out_tmp = os.path.join(tmp, "libmoe_route.so")
         cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", out_tmp, *objs]
         if verbose:

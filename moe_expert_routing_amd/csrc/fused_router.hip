@@ -25,15 +25,15 @@
 //     that both fragment reads are free of bank conflicts.
 // After the last step the fp32 logits (soft-capped when asked) go to LDS and
 // the same routing core as
-// the standalone kernel (route_tile.cuh) routes the 32 rows, 8 lanes per row.
+// the standalone kernel (route_tile.hpp) routes the 32 rows, 8 lanes per row.
 // The logits never leave the compute unit.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 #include "route_internal.h"
-#include "route_tile.cuh"
+#include "route_tile.hpp"
 
 namespace moe_route {
 namespace {
@@ -266,7 +266,7 @@ __device__ __forceinline__ bool fr_project(const uint16_t* __restrict__ hidden,
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
-    const float* __restrict__ bias, int64_t M, int H, int TG, int K, int renorm, float cap,
+    BiasRef bias, int64_t M, int H, int TG, int K, int renorm, float cap,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     __shared__ __align__(1024) unsigned char sA[kFrAStages][kFrABytes];
     __shared__ __align__(1024) unsigned char sW[kFrWStages][kFrWBytes];
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
             L[m * kFrE + n] = cap != 0.0f ? cap * tanh_f32(acc[0][nt][j] / cap) : acc[0][nt][j];
         }
     }
-    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
+    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias_at(bias, t);
     __syncthreads();
     if (copier) return;
 
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kFrStepThreads) void fused_router_step_kernel(
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     const float* __restrict__ part, int64_t M, int nsplit, float cap,
-    const float* __restrict__ bias, int TG, int K, int renorm, float* __restrict__ w_out,
+    BiasRef bias, int TG, int K, int renorm, float* __restrict__ w_out,
     int32_t* __restrict__ id_out) {
     __shared__ float4 red[16][64];
     __shared__ __align__(16) float L[kFrE];         // the row's logits
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
         a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
     }
     red[q][c4] = a;
-    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias[t];
+    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias_at(bias, t);
     __syncthreads();
     if (q == 0) {
 #pragma unroll
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
 template <bool SOFTMAX, bool BIAS, int GRP>
 __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     const float* __restrict__ part, int64_t M, int nsplit, float cap,
-    const float* __restrict__ bias, int TG, int K, int renorm, float* __restrict__ w_out,
+    BiasRef bias, int TG, int K, int renorm, float* __restrict__ w_out,
     int32_t* __restrict__ id_out) {
     __shared__ __align__(16) float S[8][kFrE];      // routing scratch of the 8 rows
     __shared__ __align__(16) float s_bias[BIAS ? kFrE : 4];
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     const int64_t rrow = row < M ? row : M - 1;
     if constexpr (BIAS) {
 #pragma unroll
-        for (int i = t; i < kFrE; i += kWave) s_bias[bias_elem<kFrE>(i)] = bias[i];
+        for (int i = t; i < kFrE; i += kWave) s_bias[bias_elem<kFrE>(i)] = bias_at(bias, i);
     }
     const int64_t split_stride = M * kFrE;
     const float* src = part + rrow * kFrE + sub * 32;
@@ -599,7 +599,7 @@ route_status_t launch_rr(const FusedProblem& f, const float* part, int nsplit) {
 route_status_t launch_reduce_route(const FusedProblem& f, const float* part, int nsplit) {
     const RouteProblem& p = f.route;
     const bool soft = p.scoring == ROUTE_SOFTMAX;
-    const bool bias = p.bias != nullptr;
+    const bool bias = p.bias.p != nullptr;
     if (p.G == 1) {
         if (soft) return launch_rr<true, false, 0>(f, part, nsplit);
         return bias ? launch_rr<false, true, 0>(f, part, nsplit)
@@ -650,10 +650,10 @@ route_status_t launch_fr(const FusedProblem& f) {
 bool fused_router_supported(const FusedProblem& f) {
     const RouteProblem& p = f.route;
     if (p.E != kFrE) return small_router_supported(f);
-    const uintptr_t a = reinterpret_cast<uintptr_t>(f.hidden) | reinterpret_cast<uintptr_t>(f.w) |
-                        reinterpret_cast<uintptr_t>(p.bias);
+    // the bias is read one entry at a time: its own alignment is enough
+    const uintptr_t a = reinterpret_cast<uintptr_t>(f.hidden) | reinterpret_cast<uintptr_t>(f.w);
     if (p.E != kFrE || f.H % kFrBK != 0 || (a % 16) != 0 || p.K > 8) return false;
-    if (p.scoring == ROUTE_SOFTMAX && p.bias != nullptr) return false;
+    if (p.scoring == ROUTE_SOFTMAX && p.bias.p != nullptr) return false;
     if (p.G == 1) return true;
     if (p.G != 8 || p.TG > 4) return false;
     // softmax with a top-2-sum group score has no specialised routing core
@@ -696,7 +696,7 @@ route_status_t launch_fused_router(const FusedProblem& f) {
         if (plan.splits > 1) return launch_split(f, plan);
     }
     const bool soft = p.scoring == ROUTE_SOFTMAX;
-    const bool bias = p.bias != nullptr;
+    const bool bias = p.bias.p != nullptr;
     if (p.G == 1) {
         if (soft) return launch_fr<true, false, 0>(f);
         return bias ? launch_fr<false, true, 0>(f) : launch_fr<false, false, 0>(f);

@@ -31,7 +31,7 @@
 
 #include <algorithm>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 #include "route_internal.h"
 
 namespace moe_route {
@@ -51,7 +51,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // selection scores c = s + bias, K picks by (c desc, index asc), weights s
 // of the picks, optionally divided by their sum (added in pick order).
 template <int E, bool SOFTMAX, bool BIAS>
-__device__ __forceinline__ void route_token(const float (&x)[E], const float* __restrict__ bias,
+__device__ __forceinline__ void route_token(const float (&x)[E], BiasRef bias,
                                             int K, int renorm, float* __restrict__ w_row,
                                             int32_t* __restrict__ id_row) {
     float s[E], c[E];
@@ -72,7 +72,7 @@ __device__ __forceinline__ void route_token(const float (&x)[E], const float* __
         for (int e = 0; e < E; ++e) s[e] = sigmoid_f32(x[e]);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) c[e] = BIAS ? s[e] + bias[e] : s[e];
+    for (int e = 0; e < E; ++e) c[e] = BIAS ? s[e] + bias_at(bias, e) : s[e];
 
     int slot[E];  // pick rank of each expert, -1 if not picked
 #pragma unroll
@@ -104,7 +104,7 @@ constexpr int kSrTokens = 8;  // tokens per group
 template <int E, bool SOFTMAX, bool BIAS>
 __global__ __launch_bounds__(kSrThreads) void small_router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
-    const float* __restrict__ bias, int64_t M, int H, int K, int renorm, float cap,
+    BiasRef bias, int64_t M, int H, int K, int renorm, float cap,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     constexpr int T = kSrTokens;
     constexpr int NS = E / 8;          // expert slices per wave
@@ -247,14 +247,8 @@ template <int E, bool SOFTMAX, bool BIAS>
 route_status_t launch_sr(const FusedProblem& f) {
     const RouteProblem& p = f.route;
     auto kernel = small_router_kernel<E, SOFTMAX, BIAS>;
-    static int resident = 0;  // blocks per CU for this instantiation
-    if (resident == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kSrThreads, 0) !=
-                hipSuccess || n <= 0)
-            n = 1;
-        resident = n;
-    }
+    // blocks per CU for this instantiation (a thread-safe one-time query)
+    static const int resident = resident_blocks(kernel, kSrThreads);
     const int64_t groups = (f.M + kSrTokens - 1) / kSrTokens;
     const int64_t blocks = std::min<int64_t>(groups, (int64_t)device_cu_count() * resident);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSrThreads), 0, p.stream,
@@ -269,7 +263,7 @@ route_status_t launch_sr(const FusedProblem& f) {
 // picks added in pick order; the pick of rank k is stored by its lane.
 template <int E, bool SOFTMAX, bool BIAS>
 __device__ __forceinline__ void route_lanes16(float x, int j, bool store,
-                                              const float* __restrict__ bias, int K, int renorm,
+                                              BiasRef bias, int K, int renorm,
                                               float* __restrict__ w_row,
                                               int32_t* __restrict__ id_row) {
     const bool live = j < E;
@@ -286,7 +280,7 @@ __device__ __forceinline__ void route_lanes16(float x, int j, bool store,
     } else {
         s = sigmoid_f32(x);
     }
-    const float c = BIAS && live ? s + bias[j] : s;
+    const float c = BIAS && live ? s + bias_at(bias, j) : s;
     bool open = live;  // not picked yet
     int rank = -1;
     float tot = 0.f;
@@ -339,7 +333,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int E, int NB, bool SOFTMAX, bool BIAS>
 __global__ __launch_bounds__(kSmThreads) void small_router_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
-    const float* __restrict__ bias, int64_t M, int H, int K, int renorm, float cap,
+    BiasRef bias, int64_t M, int H, int K, int renorm, float cap,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     __shared__ float part[kSmWaves][kSmTile * 16];
     __shared__ __align__(16) unsigned char wstage[kSmWaves][kSmBatch * 1024];
@@ -505,10 +499,10 @@ route_status_t launch_sr_e(const FusedProblem& f) {
     const bool mfma = f.H <= kSmHMax && (E == 16 || f.M >= 256 * kSmTile);
     if (mfma) {
         if (p.scoring == ROUTE_SOFTMAX) return launch_sm<E, true, false>(f);
-        return p.bias ? launch_sm<E, false, true>(f) : launch_sm<E, false, false>(f);
+        return p.bias.p ? launch_sm<E, false, true>(f) : launch_sm<E, false, false>(f);
     }
     if (p.scoring == ROUTE_SOFTMAX) return launch_sr<E, true, false>(f);
-    return p.bias ? launch_sr<E, false, true>(f) : launch_sr<E, false, false>(f);
+    return p.bias.p ? launch_sr<E, false, true>(f) : launch_sr<E, false, false>(f);
 }
 
 }  // namespace
@@ -518,7 +512,7 @@ bool small_router_supported(const FusedProblem& f) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(f.hidden) | reinterpret_cast<uintptr_t>(f.w);
     if ((p.E != 8 && p.E != 16) || f.H % 8 != 0 || (a % 16) != 0) return false;
     if (p.G != 1) return false;
-    return !(p.scoring == ROUTE_SOFTMAX && p.bias != nullptr);
+    return !(p.scoring == ROUTE_SOFTMAX && p.bias.p != nullptr);
 }
 
 route_status_t launch_small_router(const FusedProblem& f) {

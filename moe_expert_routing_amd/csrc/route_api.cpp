@@ -24,14 +24,43 @@ route_status_t check_shape(int64_t M, int E, int K, int G, int TG, route_group_s
     return ROUTE_OK;
 }
 
-route_status_t check_io(const void* logits, route_dtype_t dtype, const float* bias, int64_t M,
-                        float* w, int32_t* ids) {
-    if (dtype != ROUTE_F32 && dtype != ROUTE_BF16) return ROUTE_EINVAL;
+bool known_dtype(route_dtype_t d) { return d == ROUTE_F32 || d == ROUTE_BF16; }
+
+route_status_t check_io(const void* logits, route_dtype_t dtype, moe_route::BiasRef bias,
+                        int64_t M, float* w, int32_t* ids) {
+    if (!known_dtype(dtype)) return ROUTE_EINVAL;
     if (M == 0) return ROUTE_OK;
     if (!logits || !w || !ids) return ROUTE_EINVAL;
     if (!aligned(logits, dtype == ROUTE_F32 ? 4 : 2) || !aligned(w, 4) || !aligned(ids, 4))
         return ROUTE_EINVAL;
-    if (bias && !aligned(bias, 4)) return ROUTE_EINVAL;
+    if (bias.p && !aligned(bias.p, bias.bf16 ? 2 : 4)) return ROUTE_EINVAL;
+    return ROUTE_OK;
+}
+
+// The bias reference of an entry point; false for an unknown bias dtype.
+bool make_bias(const void* bias, route_dtype_t bias_dtype, moe_route::BiasRef& out) {
+    out = moe_route::BiasRef{bias, bias_dtype == ROUTE_BF16 ? 1 : 0};
+    return known_dtype(bias_dtype);
+}
+
+// Checks shared by the dispatch entry points; sets d.n = num_tokens * top_k.
+route_status_t check_dispatch(moe_route::DispatchProblem& d, const float* topk_weights,
+                              int64_t num_tokens, int32_t top_k) {
+    if (num_tokens < 0 || top_k < 1 || d.E < 1) return ROUTE_EINVAL;
+    if (d.E > moe_route::kMaxExperts) return ROUTE_ENOTSUP;
+    if (num_tokens > (int64_t(1) << 31) / top_k ||
+        num_tokens * top_k >= (int64_t(1) << 31)) return ROUTE_ENOTSUP;
+    d.n = num_tokens * top_k;
+    if (!d.counts || !d.offsets) return ROUTE_EINVAL;
+    if (!aligned(d.counts, 4) || !aligned(d.offsets, 4)) return ROUTE_EINVAL;
+    if (d.sorted_weights && !topk_weights) return ROUTE_EINVAL;
+    if (d.n > 0) {
+        if (!d.ids || !d.gather || !d.scatter) return ROUTE_EINVAL;
+        if (!aligned(d.ids, 4) || !aligned(d.gather, 4) || !aligned(d.scatter, 4))
+            return ROUTE_EINVAL;
+        if (d.sorted_weights && (!aligned(d.sorted_weights, 4) || !aligned(topk_weights, 4)))
+            return ROUTE_EINVAL;
+    }
     return ROUTE_OK;
 }
 
@@ -52,7 +81,7 @@ route_status_t route_topk_softmax(const void* gating_output, route_dtype_t dtype
                                   int64_t num_tokens, int32_t num_experts, int32_t top_k,
                                   int32_t renormalize, float* topk_weights, int32_t* topk_ids,
                                   void* stream) {
-    RouteProblem p{gating_output, dtype, nullptr, num_tokens, num_experts, top_k, 1, 1,
+    RouteProblem p{gating_output, dtype, {nullptr, 0}, num_tokens, num_experts, top_k, 1, 1,
                    ROUTE_SOFTMAX, ROUTE_GROUP_MAX, renormalize != 0, topk_weights, topk_ids,
                    static_cast<hipStream_t>(stream)};
     return route_common(p);
@@ -63,19 +92,21 @@ route_status_t route_grouped_topk(const void* gating_output, route_dtype_t dtype
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, route_scoring_t scoring_func,
                                   float* topk_weights, int32_t* topk_ids, void* stream) {
-    RouteProblem p{gating_output, dtype, nullptr, num_tokens, num_experts, top_k,
+    RouteProblem p{gating_output, dtype, {nullptr, 0}, num_tokens, num_experts, top_k,
                    num_expert_group, topk_group, scoring_func, ROUTE_GROUP_MAX,
                    renormalize != 0, topk_weights, topk_ids, static_cast<hipStream_t>(stream)};
     return route_common(p);
 }
 
 route_status_t route_biased_grouped_topk(const void* gating_output, route_dtype_t dtype,
-                                         const float* correction_bias, int64_t num_tokens,
-                                         int32_t num_experts, int32_t top_k,
+                                         const void* correction_bias, route_dtype_t bias_dtype,
+                                         int64_t num_tokens, int32_t num_experts, int32_t top_k,
                                          int32_t num_expert_group, int32_t topk_group,
                                          int32_t renormalize, float* topk_weights,
                                          int32_t* topk_ids, void* stream) {
-    RouteProblem p{gating_output, dtype, correction_bias, num_tokens, num_experts, top_k,
+    moe_route::BiasRef bias;
+    if (!make_bias(correction_bias, bias_dtype, bias)) return ROUTE_EINVAL;
+    RouteProblem p{gating_output, dtype, bias, num_tokens, num_experts, top_k,
                    num_expert_group, topk_group, ROUTE_SIGMOID, ROUTE_GROUP_TOP2_SUM,
                    renormalize != 0, topk_weights, topk_ids, static_cast<hipStream_t>(stream)};
     return route_common(p);
@@ -90,8 +121,9 @@ size_t route_fused_router_workspace_size(int64_t num_tokens, int32_t hidden_dim,
 
 route_status_t route_fused_router(const void* hidden_states, const void* router_weight,
                                   int64_t num_tokens, int32_t hidden_dim, int32_t num_experts,
-                                  route_scoring_t scoring_func, const float* correction_bias,
-                                  route_group_score_t group_score, int32_t top_k,
+                                  route_scoring_t scoring_func, const void* correction_bias,
+                                  route_dtype_t bias_dtype, route_group_score_t group_score,
+                                  int32_t top_k,
                                   int32_t num_expert_group, int32_t topk_group,
                                   int32_t renormalize, float logit_softcap,
                                   float* topk_weights, int32_t* topk_ids, void* workspace,
@@ -103,19 +135,23 @@ route_status_t route_fused_router(const void* hidden_states, const void* router_
     if (st != ROUTE_OK) return st;
     if (scoring_func != ROUTE_SOFTMAX && scoring_func != ROUTE_SIGMOID) return ROUTE_EINVAL;
     if (hidden_dim < 1) return ROUTE_EINVAL;
-    st = check_io(hidden_states, ROUTE_BF16, correction_bias, num_tokens, topk_weights, topk_ids);
+    moe_route::BiasRef bias;
+    if (!make_bias(correction_bias, bias_dtype, bias)) return ROUTE_EINVAL;
+    st = check_io(hidden_states, ROUTE_BF16, bias, num_tokens, topk_weights, topk_ids);
     if (st != ROUTE_OK) return st;
     if (num_tokens > 0 && (!router_weight || !aligned(router_weight, 2))) return ROUTE_EINVAL;
     if (workspace == nullptr ? workspace_bytes != 0 : !aligned(workspace, 16))
         return ROUTE_EINVAL;
     FusedProblem f{hidden_states, router_weight, num_tokens, hidden_dim, logit_softcap, nullptr,
-                   RouteProblem{nullptr, ROUTE_BF16, correction_bias, num_tokens, num_experts,
+                   RouteProblem{nullptr, ROUTE_BF16, bias, num_tokens, num_experts,
                                 top_k, num_expert_group, topk_group, scoring_func, group_score,
                                 renormalize != 0, topk_weights, topk_ids,
                                 static_cast<hipStream_t>(stream)}};
     if (!moe_route::fused_router_supported(f)) return ROUTE_ENOTSUP;
     if (workspace != nullptr) {
-        if (workspace_bytes < moe_route::fused_router_workspace_bytes(num_tokens, hidden_dim))
+        // the size this shape asks for (0 for 8 or 16 experts: none is used)
+        if (workspace_bytes <
+            route_fused_router_workspace_size(num_tokens, hidden_dim, num_experts))
             return ROUTE_EINVAL;
         f.workspace = static_cast<float*>(workspace);
     }
@@ -137,27 +173,15 @@ route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* top
                                        int32_t* gather_idx, int32_t* scatter_idx,
                                        float* sorted_weights, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-    if (num_tokens < 0 || top_k < 1 || num_experts < 1) return ROUTE_EINVAL;
-    if (num_experts > moe_route::kMaxExperts) return ROUTE_ENOTSUP;
-    if (num_tokens > (int64_t(1) << 31) / top_k ||
-        num_tokens * top_k >= (int64_t(1) << 31)) return ROUTE_ENOTSUP;
-    const int64_t n = num_tokens * top_k;
-    if (!expert_counts || !expert_offsets || !workspace) return ROUTE_EINVAL;
-    if (!aligned(expert_counts, 4) || !aligned(expert_offsets, 4) || !aligned(workspace, 4))
-        return ROUTE_EINVAL;
-    if (workspace_bytes < moe_route::dispatch_workspace_bytes(n, num_experts)) return ROUTE_EINVAL;
-    if (sorted_weights && !topk_weights) return ROUTE_EINVAL;
-    if (n > 0) {
-        if (!topk_ids || !gather_idx || !scatter_idx) return ROUTE_EINVAL;
-        if (!aligned(topk_ids, 4) || !aligned(gather_idx, 4) || !aligned(scatter_idx, 4))
-            return ROUTE_EINVAL;
-        if (sorted_weights && (!aligned(sorted_weights, 4) || !aligned(topk_weights, 4)))
-            return ROUTE_EINVAL;
-    }
-    moe_route::DispatchProblem d{topk_ids, sorted_weights ? topk_weights : nullptr, n,
+    moe_route::DispatchProblem d{topk_ids, sorted_weights ? topk_weights : nullptr, 0,
                                  num_experts, expert_counts, expert_offsets, gather_idx,
                                  scatter_idx, sorted_weights, workspace,
                                  static_cast<hipStream_t>(stream)};
+    route_status_t st = check_dispatch(d, topk_weights, num_tokens, top_k);
+    if (st != ROUTE_OK) return st;
+    if (!workspace || !aligned(workspace, 4)) return ROUTE_EINVAL;
+    if (workspace_bytes < moe_route::dispatch_workspace_bytes(d.n, num_experts))
+        return ROUTE_EINVAL;
     return moe_route::launch_dispatch(d);
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "route_internal.h"
+
 namespace moe_route {
 
 constexpr int kWave = 64;
@@ -11,6 +13,22 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
+}
+
+// Entry i of a correction bias, widened to fp32 (exactly, for bf16).
+__device__ __forceinline__ float bias_at(const BiasRef& b, int i) {
+    return b.bf16 ? bf16_bits_to_float(static_cast<const uint16_t*>(b.p)[i])
+                  : static_cast<const float*>(b.p)[i];
+}
+// Entries 4i .. 4i+3 of a correction bias: one 16-byte load (fp32) or one
+// 8-byte load (bf16, widened exactly).
+__device__ __forceinline__ float4 bias4_at(const BiasRef& b, int i) {
+    if (b.bf16) {
+        const uint2 u = static_cast<const uint2*>(b.p)[i];
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+    }
+    return static_cast<const float4*>(b.p)[i];
 }
 
 // v_exp_f32 computes 2^x; v_rcp_f32 is the hardware reciprocal (1 ulp).

@@ -27,7 +27,7 @@
 //             atomics.
 #include <hip/hip_runtime.h>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 #include "route_internal.h"
 
 namespace moe_route {

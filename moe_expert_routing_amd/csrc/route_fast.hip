@@ -31,8 +31,10 @@
 // exact (value, index) comparisons on the fp32 scores.
 #include <hip/hip_runtime.h>
 
-#include "route_common.cuh"
-#include "route_tile.cuh"
+#include <atomic>
+
+#include "route_common.hpp"
+#include "route_tile.hpp"
 #include "route_internal.h"
 
 namespace moe_route {
@@ -89,8 +91,8 @@ struct RawLane<float, VPL> {
 template <typename T, int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/,
           int SPLIT, int TL, int KMAX>
 __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
-    const T* __restrict__ logits, const float* __restrict__ bias, int64_t M, int TG, int K,
-    int renorm, float* __restrict__ w_out, int32_t* __restrict__ id_out) {
+    const T* __restrict__ logits, BiasRef bias, int64_t M, int TG, int K, int renorm,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     constexpr int E = LPR * VPL;
     constexpr int RPW = kWave / LPR;               // rows per wave
     static_assert(GRP == 0 || VPL % SPLIT == 0, "a group splits evenly");
@@ -118,12 +120,13 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
         const int64_t row = min(t * RPW + rw, M - 1);
         r.load(logits + row * E + sub * VPL);
     };
-    // The bias (one float4 per lane) is requested before the first tile, so
-    // that the prologue below needs only the bias to have arrived.
-    static_assert(!BIAS || E <= 4 * kWave, "one float4 of bias per lane");
+    // The bias (four entries per lane, fp32 or bf16) is requested before the
+    // first tile, so that the prologue below needs only the bias to have
+    // arrived.
+    static_assert(!BIAS || E <= 4 * kWave, "four bias entries per lane");
     const bool has_b = BIAS && 4 * lane < E;
     float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_b) bq = *reinterpret_cast<const float4*>(bias + 4 * lane);
+    if (has_b) bq = bias4_at(bias, lane);
     RawLane<T, VPL> ra, rb;  // ping-pong: one tile routed while the next loads
     // In flight during the prologue below.  A wave without a tile loads the
     // last one anyway: with the load unconditional, the prologue's wait
@@ -176,14 +179,8 @@ route_status_t launch_fast(const RouteProblem& p) {
     constexpr int RPW = kWave / LPR;
     auto kernel = route_fast_kernel<T, LPR, VPL, SOFTMAX, BIAS, GRP, SPLIT, TL, KMAX>;
     // Persistent grid: every block resident at once, tiles strided over them.
-    static int resident = 0;  // blocks per CU for this instantiation
-    if (resident == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kWavesPerBlock * kWave, 0) !=
-                hipSuccess || n <= 0)
-            n = 1;
-        resident = n;
-    }
+    // Blocks per CU for this instantiation (a thread-safe one-time query).
+    static const int resident = resident_blocks(kernel, kWavesPerBlock * kWave);
     const int64_t tiles = (p.M + RPW - 1) / RPW;
     int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t cap = (int64_t)device_cu_count() * resident;
@@ -207,7 +204,7 @@ route_status_t dispatch_lpr8_k(const RouteProblem& p, bool& handled) {
     constexpr int TLG = KMAX < 4 ? KMAX : 4;  // list length, grouped
     handled = true;
     const bool soft = p.scoring == ROUTE_SOFTMAX;
-    const bool bias = p.bias != nullptr;
+    const bool bias = p.bias.p != nullptr;
     if (p.G == 1) {
         if (soft) return launch_fast<T, 8, VPL, true, false, 0, 1, TLU, KMAX>(p);
         if (bias) return launch_fast<T, 8, VPL, false, true, 0, 1, TLU, KMAX>(p);
@@ -237,23 +234,26 @@ route_status_t dispatch_lpr8(const RouteProblem& p, bool& handled) {
 }  // namespace
 
 int device_cu_count() {
-    static int cached[64] = {0};
+    // Per-device cache; concurrent first calls may both query, and store the
+    // same value.
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 route_status_t launch_route(const RouteProblem& p) {
     const size_t esz = p.dtype == ROUTE_F32 ? 4 : 2;
     const bool vec_ok = aligned16(p.logits) && ((size_t)p.E * esz) % 16 == 0 &&
-                        (p.bias == nullptr || aligned16(p.bias));
+                        (p.bias.p == nullptr ||
+                         (reinterpret_cast<uintptr_t>(p.bias.p) % (p.bias.bf16 ? 8 : 16)) == 0);
     bool handled = false;
     route_status_t st = ROUTE_OK;
     if (vec_ok) {
@@ -266,7 +266,7 @@ route_status_t launch_route(const RouteProblem& p) {
             handled = true;
             if (p.scoring == ROUTE_SOFTMAX)
                 st = launch_fast<float, 1, 8, true, false, 0, 1, 2, 2>(p);
-            else if (p.bias)
+            else if (p.bias.p)
                 st = launch_fast<float, 1, 8, false, true, 0, 1, 2, 2>(p);
             else
                 st = launch_fast<float, 1, 8, false, false, 0, 1, 2, 2>(p);

@@ -10,7 +10,7 @@
 // optional renormalisation (sections 2 and 4).
 #include <hip/hip_runtime.h>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 #include "route_internal.h"
 
 namespace moe_route {
@@ -29,7 +29,7 @@ __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t* p, int i) 
 
 template <typename T, bool SOFTMAX, bool TOP2>
 __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
-    const T* __restrict__ logits, const float* __restrict__ bias, int64_t M, int E, int G,
+    const T* __restrict__ logits, BiasRef bias, int64_t M, int E, int G,
     int TG, int K, int renorm, float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     __shared__ float s_score[kGenericWaves][kMaxExperts];   // unbiased score s
     __shared__ float s_choice[kGenericWaves][kMaxExperts];  // selection score c
@@ -61,13 +61,13 @@ __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
             for (int e = lane; e < E; e += kWave) {
                 float s = sc[e] / sum;
                 sc[e] = s;
-                ch[e] = s + (bias ? bias[e] : 0.f);
+                ch[e] = s + (bias.p ? bias_at(bias, e) : 0.f);
             }
         } else {
             for (int e = lane; e < E; e += kWave) {
                 float s = sigmoid_f32(load_logit(xr, e));
                 sc[e] = s;
-                ch[e] = s + (bias ? bias[e] : 0.f);
+                ch[e] = s + (bias.p ? bias_at(bias, e) : 0.f);
             }
         }
         wave_lds_sync();
@@ -107,6 +107,9 @@ __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
                 if (beats(v, e, bv, bi)) { bv = v; bi = e; }
             }
             wave_argmax(bv, bi);
+            // bi keeps its sentinel only when no candidate beats -inf (NaN
+            // scores): the output is then unspecified, but stays inside the row
+            bi = min(max(bi, 0), E - 1);
             if (lane == k) { my_id = bi; my_w = sc[bi]; }
             if (lane == (bi % kWave)) ch[bi] = -INFINITY;  // taken
             wave_lds_sync();

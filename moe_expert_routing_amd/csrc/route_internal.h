@@ -8,11 +8,18 @@
 
 namespace moe_route {
 
+// A per-expert correction bias of E entries, float32 or bfloat16 (the
+// aiter-style call passes it in the logits' dtype).  p == nullptr: no bias.
+struct BiasRef {
+    const void* p;
+    int bf16;  // 0: float32 entries, 1: bfloat16 entries
+};
+
 // One routing problem after host-side validation.
 struct RouteProblem {
     const void* logits;     // [M, E] f32 or bf16
     route_dtype_t dtype;
-    const float* bias;      // [E] or nullptr
+    BiasRef bias;           // [E]; bias.p == nullptr: none
     int64_t M;
     int E, K, G, TG;
     route_scoring_t scoring;
@@ -53,6 +60,18 @@ constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 64;
 
 int device_cu_count();  // compute units of the current device (cached)
+
+// Blocks of `kernel` that fit on one compute unit at `threads` per block (1
+// if the query fails).  Callers keep it in a function-local static, whose
+// initialisation C++ makes thread-safe.
+template <typename F>
+int resident_blocks(F kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess ||
+        n <= 0)
+        n = 1;
+    return n;
+}
 
 // Kernel launchers (route_kernels.hip / fused_router.hip).  They assume a
 // validated problem with M > 0 and return ROUTE_OK or ROUTE_ELAUNCH.

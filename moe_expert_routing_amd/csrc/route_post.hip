@@ -17,7 +17,7 @@
 // before any is stored.
 #include <hip/hip_runtime.h>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 #include "route_internal.h"
 
 namespace moe_route {

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "route_common.cuh"
+#include "route_common.hpp"
 
 namespace moe_route {
 

@@ -9,6 +9,20 @@ import moe_expert_routing_amd as mr
 import oracle
 
 
+def oracle_router_logits(hidden, w, chunk=64):
+    """The oracle's exact router logits of every row, computed in row chunks
+    on a pool of host threads (the oracle's C routine releases the GIL); the
+    arithmetic is the oracle's own, row by row."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    M = hidden.shape[0]
+    starts = range(0, M, chunk)
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda s: oracle.router_logits(hidden[s:s + chunk], w), starts))
+    return np.concatenate(parts, axis=0) if parts else np.empty((0, w.shape[1]))
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()

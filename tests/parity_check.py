@@ -23,6 +23,10 @@ import oracle
 W_TOL = 1e-5
 TIE = 1e-6
 
+# Reports of the comparisons that named a workload (compare(..., label=...)),
+# in call order; tests/conftest.py prints them at the end of the session.
+REPORTS: list = []
+
 
 @dataclasses.dataclass
 class ParityReport:
@@ -39,6 +43,12 @@ class ParityReport:
 
     def ok(self):
         return not self.failures
+
+    @property
+    def strict_ok(self):
+        """The stricter rule: the only accepted differences are near ties at
+        the K boundary (no order or group-boundary swaps)."""
+        return self.ok() and self.near_tie_order == 0 and self.near_tie_group == 0
 
     def summary(self):
         return (f"rows={self.rows} exact={self.exact} near_tie(K={self.near_tie_k}, "
@@ -83,8 +93,9 @@ def _valid_within(row_logits, ids, w, *, scoring, bias, G, TG, rule, K, renorm):
 
 
 def compare(logits, w_gpu, ids_gpu, *, scoring, bias=None, G=1, TG=1, rule=oracle.GROUP_MAX,
-            K, renorm, oracle_out=None, rows=None):
-    """Compare GPU outputs with the oracle on every row (or the given rows)."""
+            K, renorm, oracle_out=None, rows=None, label=None):
+    """Compare GPU outputs with the oracle on every row (or the given rows).
+    With a label, the report is also kept in REPORTS for the session summary."""
     logits = np.asarray(logits)
     w_gpu = np.asarray(w_gpu)
     ids_gpu = np.asarray(ids_gpu)
@@ -119,4 +130,6 @@ def compare(logits, w_gpu, ids_gpu, *, scoring, bias=None, G=1, TG=1, rule=oracl
             rep.near_tie_k += 1
         else:
             rep.near_tie_order += 1
+    if label is not None:
+        REPORTS.append((label, rep))
     return rep

@@ -44,8 +44,13 @@ def test_status_strings():
     assert mr.status_str(99).startswith("unknown")
 
 
-def bgt(M=4, E=256, K=8, G=8, TG=4, logits=P, dtype=mr.ROUTE_BF16, bias=R, w=Q, ids=R):
-    return mr.lib().route_biased_grouped_topk(logits, dtype, bias, M, E, K, G, TG, 1, w, ids, None)
+F = mr.ROUTE_F32
+
+
+def bgt(M=4, E=256, K=8, G=8, TG=4, logits=P, dtype=mr.ROUTE_BF16, bias=R, bias_dtype=F, w=Q,
+        ids=R):
+    return mr.lib().route_biased_grouped_topk(logits, dtype, bias, bias_dtype, M, E, K, G, TG, 1,
+                                              w, ids, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -63,6 +68,11 @@ def bgt(M=4, E=256, K=8, G=8, TG=4, logits=P, dtype=mr.ROUTE_BF16, bias=R, w=Q, 
     (dict(logits=ctypes.c_void_p(0x10001)), mr.ROUTE_EINVAL),  # misaligned bf16
     (dict(w=ctypes.c_void_p(0x20002)), mr.ROUTE_EINVAL),
     (dict(bias=ctypes.c_void_p(0x30001)), mr.ROUTE_EINVAL),
+    (dict(bias=ctypes.c_void_p(0x30002)), mr.ROUTE_EINVAL),   # fp32 bias needs 4 bytes
+    (dict(bias=ctypes.c_void_p(0x30001), bias_dtype=mr.ROUTE_BF16), mr.ROUTE_EINVAL),
+    (dict(bias_dtype=7), mr.ROUTE_EINVAL),                    # unknown bias dtype
+    (dict(bias=NULL, bias_dtype=-1), mr.ROUTE_EINVAL),        # ... also with no bias
+    (dict(M=0, bias_dtype=7), mr.ROUTE_EINVAL),
     (dict(dtype=7), mr.ROUTE_EINVAL),
     (dict(E=2048, G=8, TG=4, K=8), mr.ROUTE_ENOTSUP),          # E beyond 1024
     (dict(E=256, G=1, TG=1, K=65), mr.ROUTE_ENOTSUP),          # K beyond 64
@@ -94,29 +104,39 @@ def test_fused_router_validation():
     L = mr.lib()
     f = L.route_fused_router
     sig, top2 = mr.ROUTE_SIGMOID, mr.ROUTE_GROUP_TOP2_SUM
-    assert f(P, Q, 8, 0, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
-    assert f(P, NULL, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, 4, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, 9, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 200, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 0, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 8, 7168, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, 4, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, F, 9, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, R, F, top2, 200, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
     # outside the compiled range
-    assert f(P, Q, 8, 7168, 128, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
-    assert f(P, Q, 8, 7000, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
-    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, top2, 8, 8, 4, 1, 0.0, NULL, NULL, NULL, 0, None) == \
+    assert f(P, Q, 8, 7168, 128, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
+    assert f(P, Q, 8, 7000, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == mr.ROUTE_ENOTSUP
+    assert f(NULL, NULL, 0, 7168, 256, sig, NULL, F, top2, 8, 8, 4, 1, 0.0, NULL, NULL, NULL, 0, None) == \
         mr.ROUTE_OK
+    # an unknown bias dtype, with or without a bias
+    assert f(P, Q, 8, 7168, 256, sig, R, 5, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, NULL, -1, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, 0, None) == \
+        mr.ROUTE_EINVAL
+    # a bf16 bias needs 2-byte alignment, an fp32 one 4
+    assert f(P, Q, 8, 7168, 256, sig, ctypes.c_void_p(0x30001), mr.ROUTE_BF16, top2, 8, 8, 4, 1,
+             0.0, Q, R, NULL, 0, None) == mr.ROUTE_EINVAL
+    assert f(P, Q, 8, 7168, 256, sig, ctypes.c_void_p(0x30002), F, top2, 8, 8, 4, 1, 0.0, Q, R,
+             NULL, 0, None) == mr.ROUTE_EINVAL
     # NaN or infinite caps
     for cap in (float("nan"), float("inf"), -float("inf")):
-        assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, cap, Q, R, NULL, 0, None) == \
+        assert f(P, Q, 8, 7168, 256, sig, R, F, top2, 8, 8, 4, 1, cap, Q, R, NULL, 0, None) == \
             mr.ROUTE_EINVAL
     # workspace: a size without a pointer, a misaligned one, one too small
     need = L.route_fused_router_workspace_size(8, 7168, 256)
     assert need > 0
     W = ctypes.c_void_p(0x40000)
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, need, None) == \
+    assert f(P, Q, 8, 7168, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, NULL, need, None) == \
         mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, ctypes.c_void_p(0x40008),
+    assert f(P, Q, 8, 7168, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, ctypes.c_void_p(0x40008),
              need, None) == mr.ROUTE_EINVAL
-    assert f(P, Q, 8, 7168, 256, sig, R, top2, 8, 8, 4, 1, 0.0, Q, R, W, need - 4, None) == \
+    assert f(P, Q, 8, 7168, 256, sig, R, F, top2, 8, 8, 4, 1, 0.0, Q, R, W, need - 4, None) == \
         mr.ROUTE_EINVAL
 
 
@@ -126,19 +146,19 @@ def test_fused_router_few_experts_range():
     f = mr.lib().route_fused_router
     sm, top2, mx = mr.ROUTE_SOFTMAX, mr.ROUTE_GROUP_TOP2_SUM, mr.ROUTE_GROUP_MAX
     ok = mr.ROUTE_OK
-    assert f(NULL, NULL, 0, 4096, 8, sm, NULL, mx, 2, 1, 1, 0, 30.0, NULL, NULL, NULL, 0,
+    assert f(NULL, NULL, 0, 4096, 8, sm, NULL, F, mx, 2, 1, 1, 0, 30.0, NULL, NULL, NULL, 0,
              None) == ok
-    assert f(NULL, NULL, 0, 4096, 16, sm, NULL, mx, 2, 1, 1, 0, 0.0, NULL, NULL, NULL, 0,
+    assert f(NULL, NULL, 0, 4096, 16, sm, NULL, F, mx, 2, 1, 1, 0, 0.0, NULL, NULL, NULL, 0,
              None) == ok
-    assert f(P, Q, 8, 4100, 8, sm, NULL, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+    assert f(P, Q, 8, 4100, 8, sm, NULL, F, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
         mr.ROUTE_ENOTSUP                                  # H % 8 != 0
-    assert f(P, Q, 8, 4096, 12, sm, NULL, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+    assert f(P, Q, 8, 4096, 12, sm, NULL, F, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
         mr.ROUTE_ENOTSUP                                  # 12 experts
-    assert f(P, Q, 8, 4096, 8, sm, NULL, top2, 2, 2, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+    assert f(P, Q, 8, 4096, 8, sm, NULL, F, top2, 2, 2, 1, 0, 0.0, Q, R, NULL, 0, None) == \
         mr.ROUTE_ENOTSUP                                  # expert groups
-    assert f(P, Q, 8, 4096, 8, sm, R, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+    assert f(P, Q, 8, 4096, 8, sm, R, F, mx, 2, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
         mr.ROUTE_ENOTSUP                                  # softmax with a bias
-    assert f(P, Q, 8, 4096, 8, sm, NULL, mx, 9, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
+    assert f(P, Q, 8, 4096, 8, sm, NULL, F, mx, 9, 1, 1, 0, 0.0, Q, R, NULL, 0, None) == \
         mr.ROUTE_EINVAL                                   # K > E
     assert mr.lib().route_fused_router_workspace_size(64, 4096, 8) == 0
 
@@ -179,6 +199,22 @@ def test_binding_has_no_cpu_fallback():
         mr.route_topk_softmax(x, 2)
     with pytest.raises(ValueError, match="must live on the GPU"):
         mr.route_biased_grouped_topk(x.bfloat16(), torch.zeros(8), 2, 2, 1)
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        mr.route_biased_grouped_topk(x.bfloat16(), torch.zeros(8, dtype=torch.bfloat16), 2)
+
+
+def test_binding_bias_dtypes():
+    """The binding passes float32 or bfloat16 biases of shape [E] and rejects
+    anything else before any device work."""
+    import torch
+    x = torch.zeros(2, 8)
+    for bad in (torch.zeros(8, dtype=torch.float16), torch.zeros(8, dtype=torch.float64),
+                torch.zeros(7), torch.zeros(2, 4)):
+        with pytest.raises(ValueError, match="correction_bias"):
+            mr.route_biased_grouped_topk(x, bad, 2)
+    assert mr._bias_code(None, 8) == mr.ROUTE_F32
+    assert mr._bias_code(torch.zeros(8), 8) == mr.ROUTE_F32
+    assert mr._bias_code(torch.zeros(8, dtype=torch.bfloat16), 8) == mr.ROUTE_BF16
 
 
 def test_dispatch_workspace_size():

@@ -23,7 +23,7 @@ def _check_workload(wl, M=None):
                        bias=None if b is None else to_device(b), renorm=wl.renormalize)
     sc, rule = oracle_args(wl.entry, wl.scoring)
     rep = compare(x, w, ids, scoring=sc, bias=b, G=wl.G, TG=wl.TG, rule=rule, K=wl.K,
-                  renorm=wl.renormalize)
+                  renorm=wl.renormalize, label=f"{wl.name} M={x.shape[0]}")
     log(f"[gpu]   {rep.summary()}")
     assert rep.ok(), rep.summary()
     # near ties must stay rare: they come only from sub-1e-6 gaps

@@ -1,6 +1,7 @@
 """GPU parity of the post-routing steps against the oracle: the shared-expert
-slot, the ascending id order, the bias rounded to the logit dtype, and the
-whole chain route -> shared slot -> dispatch metadata."""
+slot, the ascending id order, the correction bias in bf16 (the logits' dtype,
+as the aiter-style call passes it), and the whole chain route -> shared slot
+-> dispatch metadata."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,8 @@ import moe_expert_routing_amd as mr
 import oracle
 from gpu_util import log, to_device
 from parity_check import compare
-from workloads import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_bias, make_logits
+from workloads import (WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_bias, make_logits,
+                       random_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,17 +50,85 @@ def test_sort_ids(M, K, hi):
     np.testing.assert_array_equal(w.cpu().numpy(), rw)
 
 
-def test_bias_rounded_to_logit_dtype():
-    """The aiter-style call casts the correction bias to the logits' dtype; a
-    bf16-rounded bias passed as float32 is the same numbers."""
-    wl = WORKLOADS["biased_grouped_e256"]
-    x = make_logits(wl, 8192)
-    b = bf16_bits_to_f32(bf16_bits_from_f32(make_bias(wl)))
-    log("[gpu] biased grouped top-k with a bf16-rounded bias")
-    w, ids = mr.route_biased_grouped_topk(to_device(x), to_device(b), 8, 8, 4, True)
+def _bf16_bias_tensor(bits, offset):
+    """bf16 bias tensor on the device; offset 1 starts it one element into a
+    larger allocation (2-byte aligned only)."""
+    t = torch.from_numpy(np.concatenate([np.zeros(offset, np.uint16), bits]).view(np.int16))
+    return t.view(torch.bfloat16).cuda()[offset:]
+
+
+def _f32_bias_tensor(b, offset):
+    """float32 bias tensor on the device; offset 1 starts it one element into
+    a larger allocation (4-byte aligned only)."""
+    return torch.from_numpy(np.concatenate([np.zeros(offset, np.float32), b])).cuda()[offset:]
+
+
+@pytest.mark.parametrize("M,E,K,G,TG,dtype,offset", [
+    (65536, 256, 8, 8, 4, "bf16", 0),   # the DeepSeek-V3 shape, 65536 tokens
+    (4096, 256, 8, 1, 1, "bf16", 0),    # the aiter call's ungrouped shape
+    (1000, 256, 8, 8, 4, "f32", 0),     # fp32 logits, bf16 bias
+    (1000, 256, 8, 8, 4, "bf16", 1),    # bias 2-byte aligned only: the generic kernel
+    (300, 384, 8, 8, 4, "bf16", 0),     # the generic kernel
+    (1000, 8, 2, 1, 1, "f32", 0),       # one lane per row (8 experts)
+])
+def test_bf16_correction_bias(M, E, K, G, TG, dtype, offset):
+    """The aiter-style call casts correction_bias to the logits' dtype and
+    passes that tensor; the library takes it as bf16 and widens it exactly,
+    so the result equals the oracle's on the widened values and is
+    bit-identical to passing those values as float32 to the same kernel (a
+    misaligned bias, bf16 or float32, takes the generic kernel)."""
+    rng = np.random.default_rng(M + E + offset)
+    if dtype == "bf16" and E == 256:
+        wl = WORKLOADS["biased_grouped_e256"]
+        x = make_logits(wl, M)
+        bias_f32 = make_bias(wl)
+    else:
+        x = random_logits(rng, M, E, dtype, std=1.5)
+        bias_f32 = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    bits = bf16_bits_from_f32(bias_f32)
+    b = bf16_bits_to_f32(bits)                     # the exact values of the bf16 bias
+    bd = _bf16_bias_tensor(bits, offset)
+    assert bd.dtype == torch.bfloat16 and (bd.data_ptr() % 8 != 0) == bool(offset)
+    log(f"[gpu] bf16 correction bias M={M} E={E} K={K} G={G} TG={TG} logits={dtype} "
+        f"offset={offset}")
+    xd = to_device(x)
+    w, ids = mr.route_biased_grouped_topk(xd, bd, K, G, TG, True)
+    w2, ids2 = mr.route_biased_grouped_topk(xd, _f32_bias_tensor(b, offset), K, G, TG, True)
     torch.cuda.synchronize()
-    rep = compare(x, w.cpu().numpy(), ids.cpu().numpy(), scoring=oracle.SIGMOID, bias=b, G=8,
-                  TG=4, rule=oracle.GROUP_TOP2SUM, K=8, renorm=True)
+    assert torch.equal(w, w2) and torch.equal(ids, ids2)
+    rep = compare(x, w.cpu().numpy(), ids.cpu().numpy(), scoring=oracle.SIGMOID, bias=b, G=G,
+                  TG=TG, rule=oracle.GROUP_TOP2SUM, K=K, renorm=True,
+                  label=f"bf16 bias M={M} E={E} G={G} logits={dtype} offset={offset}")
+    log(f"[gpu]   {rep.summary()}")
+    assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("M,H,E,K,G,TG,workspace", [
+    (130, 512, 256, 8, 8, 4, False),    # one fused kernel
+    (130, 2048, 256, 8, 8, 4, None),    # split path: a block per row
+    (3000, 640, 256, 8, 8, 4, None),    # split path: a wave per 8 rows
+    (300, 2048, 16, 4, 1, 1, None),     # 16 experts
+])
+def test_bf16_correction_bias_fused_router(M, H, E, K, G, TG, workspace):
+    """A bf16 correction bias on every fused-router path."""
+    rng = np.random.default_rng(M * 3 + H + E)
+    hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32))
+    wr = bf16_bits_from_f32(rng.standard_normal((H, E), dtype=np.float32) *
+                            np.float32(H ** -0.5))
+    bits = bf16_bits_from_f32((rng.standard_normal(E) * 0.1).astype(np.float32))
+    b = bf16_bits_to_f32(bits)
+    log(f"[gpu] bf16 correction bias, fused router M={M} H={H} E={E} "
+        f"{'one kernel' if workspace is False else 'default'}")
+    hd, wd = to_device(hidden), to_device(wr)
+    w, ids = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid",
+                                   _bf16_bias_tensor(bits, 0), "top2sum", workspace=workspace)
+    w2, ids2 = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid", to_device(b), "top2sum",
+                                     workspace=workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(w, w2) and torch.equal(ids, ids2)
+    logits = oracle.router_logits(hidden, wr)
+    rep = compare(logits, w.cpu().numpy(), ids.cpu().numpy(), scoring=oracle.SIGMOID, bias=b,
+                  G=G, TG=TG, rule=oracle.GROUP_TOP2SUM, K=K, renorm=True)
     log(f"[gpu]   {rep.summary()}")
     assert rep.ok(), rep.summary()
 

@@ -7,7 +7,7 @@ import torch
 
 import moe_expert_routing_amd as mr
 import oracle
-from gpu_util import log, to_device
+from gpu_util import log, oracle_router_logits, to_device
 from parity_check import compare
 from workloads import WORKLOADS, bf16_bits_from_f32, make_router_inputs
 
@@ -24,18 +24,17 @@ def _inputs(rng, M, H, E, scale=1.0, bias=False):
     return hidden, w, b
 
 
-def _run_check(hidden, w, b, E, K, scoring, renorm, cap, rows=None):
+def _run_check(hidden, w, b, E, K, scoring, renorm, cap, label=None, workspace=None):
     wt, ids = mr.route_fused_router(to_device(hidden), to_device(w), K, 1, 1, renorm, scoring,
                                     None if b is None else to_device(b), "max",
-                                    logit_softcap=cap)
+                                    logit_softcap=cap, workspace=workspace)
     torch.cuda.synchronize()
     wt, ids = wt.cpu().numpy(), ids.cpu().numpy()
-    rows = np.arange(hidden.shape[0]) if rows is None else rows
-    logits = oracle.router_logits(hidden[rows], w)
+    logits = oracle_router_logits(hidden, w)
     if cap:
         logits = oracle.softcap(logits, cap)
-    rep = compare(logits, wt[rows], ids[rows], scoring=SC[scoring], bias=b, G=1, TG=1,
-                  rule=oracle.GROUP_MAX, K=K, renorm=renorm)
+    rep = compare(logits, wt, ids, scoring=SC[scoring], bias=b, G=1, TG=1,
+                  rule=oracle.GROUP_MAX, K=K, renorm=renorm, label=label)
     log(f"[gpu]   {rep.summary()}")
     assert rep.ok(), rep.summary()
     return wt, ids
@@ -69,21 +68,31 @@ def test_small_router(M, H, E, K, scoring, bias, renorm, cap, scale):
 
 
 @pytest.mark.parametrize("name", ["fused_router_e8_h4096", "fused_router_e16_h6144"])
-def test_small_router_workload_sampled(name):
+def test_small_router_workload(name):
+    """The full 8192-token workload, every row against the oracle."""
     wl = WORKLOADS[name]
     hidden, w = make_router_inputs(wl)
     log(f"[gpu] route_fused_router workload={wl.name} M={wl.M} H={wl.hidden_dim}")
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([np.arange(24), np.arange(wl.M - 24, wl.M),
-                                     rng.choice(wl.M, 200, replace=False)]))
     wt, ids = _run_check(hidden, w, None, wl.E, wl.K, wl.scoring, wl.renormalize, wl.softcap,
-                         rows)
+                         label=f"{wl.name} M={wl.M}")
     # every row: distinct ids in range, softmax weights in (0, 1], descending
     srt = np.sort(ids, axis=1)
     assert np.all((ids >= 0) & (ids < wl.E)) and np.all(srt[:, 1:] != srt[:, :-1])
     assert np.all((wt > 0) & (wt <= 1)) and np.all(wt[:, :-1] >= wt[:, 1:])
     if wl.renormalize:
         np.testing.assert_allclose(wt.astype(np.float64).sum(1), 1.0, atol=1e-5)
+
+
+def test_small_router_ignores_a_workspace():
+    """8 or 16 experts use no workspace; one passed anyway is accepted and
+    changes nothing."""
+    rng = np.random.default_rng(23)
+    hidden, w, _ = _inputs(rng, 64, 4096, 8)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    log("[gpu] route_fused_router E=8 M=64 H=4096 with a 64 KiB workspace")
+    a = _run_check(hidden, w, None, 8, 2, "softmax", False, 30.0, workspace=ws)
+    c = _run_check(hidden, w, None, 8, 2, "softmax", False, 30.0, workspace=False)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
 
 
 def test_small_router_deterministic():
