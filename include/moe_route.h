@@ -63,7 +63,8 @@ typedef enum {
     ROUTE_OK = 0,
     ROUTE_EINVAL = 1,
     ROUTE_ENOTSUP = 2,
-    ROUTE_ELAUNCH = 3
+    ROUTE_ELAUNCH = 3,
+    ROUTE_ETOOBIG = 4  /* larger than a static scratch buffer (noalloc entry points) */
 } route_status_t;
 
 /* Element type of the router logits / hidden states. */
@@ -225,6 +226,31 @@ route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* top
                                        int32_t* gather_idx, int32_t* scatter_idx,
                                        float* sorted_weights, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * route_dispatch_metadata without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same outputs, bit for bit, with the
+ * scratch taken from a static device buffer of the library instead of a
+ * caller workspace.  The entry point allocates nothing and frees nothing.
+ *   Limit: route_dispatch_workspace_size(num_tokens, top_k, num_experts)
+ *          must not exceed 4 MiB (e.g. up to 8,386,560 assignments at 256
+ *          experts, 2,095,104 at 1024); larger problems return
+ *          ROUTE_ETOOBIG before any GPU work.
+ *   The buffer is one per device, held until the process ends, and shared
+ *   by every call on that device: calls on one device whose executions
+ *   overlap (different streams without ordering between them) race on it.
+ *   Calls on one stream are ordered and safe.  Nothing in the buffer needs
+ *   to start at zero: every call overwrites what it reads.
+ * Other arguments and errors as route_dispatch_metadata; ROUTE_ELAUNCH also
+ * when the buffer's device address cannot be looked up.
+ */
+route_status_t route_dispatch_metadata_noalloc(const int32_t* topk_ids,
+                                               const float* topk_weights, int64_t num_tokens,
+                                               int32_t top_k, int32_t num_experts,
+                                               int32_t* expert_counts, int32_t* expert_offsets,
+                                               int32_t* gather_idx, int32_t* scatter_idx,
+                                               float* sorted_weights, void* stream);
 
 /*
  * Shared-expert slot ([ROUTING] section 6), in place on a routing result:

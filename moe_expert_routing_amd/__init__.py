@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
 
-ROUTE_OK, ROUTE_EINVAL, ROUTE_ENOTSUP, ROUTE_ELAUNCH = 0, 1, 2, 3
+ROUTE_OK, ROUTE_EINVAL, ROUTE_ENOTSUP, ROUTE_ELAUNCH, ROUTE_ETOOBIG = 0, 1, 2, 3, 4
 ROUTE_F32, ROUTE_BF16 = 0, 1
 ROUTE_SOFTMAX, ROUTE_SIGMOID = 0, 1
 ROUTE_GROUP_MAX, ROUTE_GROUP_TOP2_SUM = 0, 1
@@ -29,6 +29,7 @@ EXPORTED = (
     "route_fused_router_workspace_size",
     "route_dispatch_metadata",
     "route_dispatch_workspace_size",
+    "route_dispatch_metadata_noalloc",
     "route_fuse_shared_expert",
     "route_sort_ids",
     "route_status_str",
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
     L.route_dispatch_metadata.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p, ctypes.c_size_t,
                                           p]
     L.route_dispatch_workspace_size.argtypes = [i64, i32, i32]
+    L.route_dispatch_metadata_noalloc.argtypes = [p, p, i64, i32, i32, p, p, p, p, p, p]
     L.route_fuse_shared_expert.argtypes = [p, p, i64, i32, p, ctypes.c_float, p]
     L.route_sort_ids.argtypes = [p, p, i64, i32, p]
     L.route_dispatch_workspace_size.restype = ctypes.c_size_t
@@ -83,7 +85,7 @@ def _check(code: int, what: str):
     if code == ROUTE_OK:
         return
     msg = f"{what}: {status_str(code)}"
-    if code in (ROUTE_EINVAL, ROUTE_ENOTSUP):
+    if code in (ROUTE_EINVAL, ROUTE_ENOTSUP, ROUTE_ETOOBIG):
         raise ValueError(msg)
     raise RouteError(msg)
 

@@ -185,6 +185,26 @@ route_status_t route_dispatch_metadata(const int32_t* topk_ids, const float* top
     return moe_route::launch_dispatch(d);
 }
 
+route_status_t route_dispatch_metadata_noalloc(const int32_t* topk_ids,
+                                               const float* topk_weights, int64_t num_tokens,
+                                               int32_t top_k, int32_t num_experts,
+                                               int32_t* expert_counts, int32_t* expert_offsets,
+                                               int32_t* gather_idx, int32_t* scatter_idx,
+                                               float* sorted_weights, void* stream) {
+    moe_route::DispatchProblem d{topk_ids, sorted_weights ? topk_weights : nullptr, 0,
+                                 num_experts, expert_counts, expert_offsets, gather_idx,
+                                 scatter_idx, sorted_weights, nullptr,
+                                 static_cast<hipStream_t>(stream)};
+    route_status_t st = check_dispatch(d, topk_weights, num_tokens, top_k);
+    if (st != ROUTE_OK) return st;
+    if (moe_route::dispatch_workspace_bytes(d.n, num_experts) >
+        moe_route::dispatch_noalloc_scratch_bytes())
+        return ROUTE_ETOOBIG;
+    d.workspace = moe_route::dispatch_noalloc_scratch();  // no allocation: a static buffer
+    if (d.workspace == nullptr) return ROUTE_ELAUNCH;
+    return moe_route::launch_dispatch(d);
+}
+
 route_status_t route_fuse_shared_expert(float* topk_weights, int32_t* topk_ids,
                                         int64_t num_tokens, int32_t top_k,
                                         const int32_t* shared_expert_ids,
@@ -220,6 +240,8 @@ const char* route_status_str(route_status_t status) {
         case ROUTE_EINVAL: return "ROUTE_EINVAL: invalid argument";
         case ROUTE_ENOTSUP: return "ROUTE_ENOTSUP: shape outside the compiled range";
         case ROUTE_ELAUNCH: return "ROUTE_ELAUNCH: kernel launch failed";
+        case ROUTE_ETOOBIG:
+            return "ROUTE_ETOOBIG: problem larger than the library's static scratch buffer";
     }
     return "unknown route_status_t";
 }

@@ -27,11 +27,21 @@
 //             atomics.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "route_common.hpp"
 #include "route_internal.h"
 
 namespace moe_route {
 namespace {
+
+// Scratch of route_dispatch_metadata_noalloc (cnt[B][E] + totals[E]), for
+// callers that cannot allocate.  Each device holds its own copy until the
+// process ends.  On the host, `scratch` names a stand-in, not a device
+// address: host code uses only the address hipGetSymbolAddress returns for
+// the current device (dispatch_noalloc_scratch below).
+constexpr size_t kNoAllocScratchInts = size_t(1) << 20;  // 4 MiB
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchInts];
 
 constexpr int kDispWaves = 8;                            // 2 per SIMD: shorter place loops
 constexpr int kDispThreads = kDispWaves * kWave;
@@ -254,6 +264,23 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
 }
 
 }  // namespace
+
+size_t dispatch_noalloc_scratch_bytes() { return sizeof(int32_t) * kNoAllocScratchInts; }
+
+void* dispatch_noalloc_scratch() {
+    // Device address of `scratch` on the current device, looked up on the
+    // first call on each device (with that device current) and kept.
+    static std::atomic<void*> addr[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 size_t dispatch_workspace_bytes(int64_t n, int E) {
     const int64_t B = (n + kBlockChunk - 1) / kBlockChunk;

@@ -87,6 +87,10 @@ struct SplitPlan {
 SplitPlan fused_router_split_plan(int64_t M, int H);
 size_t fused_router_workspace_bytes(int64_t M, int H);
 size_t dispatch_workspace_bytes(int64_t n, int E);
+// The static scratch of route_dispatch_metadata_noalloc: its size, and its
+// device address on the current device (nullptr if the lookup fails).
+size_t dispatch_noalloc_scratch_bytes();
+void* dispatch_noalloc_scratch();
 route_status_t launch_dispatch(const DispatchProblem& d);
 route_status_t launch_fuse_shared(float* w, int32_t* ids, int64_t M, int K,
                                   const int32_t* shared_ids, float rsf, hipStream_t stream);

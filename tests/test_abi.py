@@ -264,6 +264,23 @@ def test_dispatch_binding_has_no_cpu_fallback():
                                    workspace=torch.zeros(64, dtype=torch.uint8))
 
 
+def test_dispatch_noalloc_validation():
+    """The allocation-free dispatch entry point: the same argument checks as
+    route_dispatch_metadata, and problems whose scratch exceeds its static
+    4 MiB buffer are refused with their own status code, all on the host."""
+    f = mr.lib().route_dispatch_metadata_noalloc
+    assert f(P, NULL, -1, 8, 256, Q, R, P, Q, NULL, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 4, 8, 1025, Q, R, P, Q, NULL, None) == mr.ROUTE_ENOTSUP
+    assert f(NULL, NULL, 4, 8, 256, Q, R, P, Q, NULL, None) == mr.ROUTE_EINVAL
+    assert f(P, NULL, 4, 8, 256, Q, R, P, Q, P, None) == mr.ROUTE_EINVAL  # weights missing
+    # 2^22 tokens x 8 slots over 1024 experts: 64 MiB of scratch
+    assert mr.route_dispatch_workspace_size(1 << 22, 8, 1024) > (4 << 20)
+    rc = f(P, NULL, 1 << 22, 8, 1024, Q, R, P, Q, NULL, None)
+    assert rc == mr.ROUTE_ETOOBIG and "static scratch" in mr.status_str(rc)
+    # the largest problem that fits: B + 1 rows of 256 counts in 4 MiB
+    assert mr.route_dispatch_workspace_size(4095 * 2048 // 8, 8, 256) == 4 << 20
+
+
 def test_post_routing_validation():
     L = mr.lib()
     f, s = L.route_fuse_shared_expert, L.route_sort_ids
