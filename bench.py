@@ -446,6 +446,76 @@ def measure_all(out_path=None):
     return results
 
 
+def profile_run(calls=5):
+    """A few calls of every workload's kernels, each on its own input set
+    where it reads enough to leave the last-level cache, with no timing
+    loops: the program profiled by the committed rocprofv3 summaries
+    (kernel traces and counter passes)."""
+    import numpy as np
+    import torch
+
+    import moe_expert_routing_amd as mr
+    from workloads import WORKLOADS, make_bias, make_logits, make_router_inputs
+    dev = torch.device("cuda", 0)
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    def sets(t, n):
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    for name in ("biased_grouped_e256", "sigmoid_bias_e256_k8", "grouped_softmax_e160",
+                 "softmax_e8_k2"):
+        wl = WORKLOADS[name]
+        xs = sets(dev_tensor(make_logits(wl)), calls)
+        b = make_bias(wl)
+        b = None if b is None else dev_tensor(b)
+        for x in xs:
+            if wl.entry == "route_topk_softmax":
+                mr.route_topk_softmax(x, wl.K, wl.renormalize)
+            elif wl.entry == "route_grouped_topk":
+                mr.route_grouped_topk(x, wl.K, wl.G, wl.TG, wl.renormalize, wl.scoring)
+            else:
+                out = mr.route_biased_grouped_topk(x, b, wl.K, wl.G, wl.TG, wl.renormalize)
+                if name == "biased_grouped_e256":
+                    w, ids = out
+        torch.cuda.synchronize()
+        eprint(f"[profile] {name}: {calls} calls")
+    # dispatch metadata of the 65536-token routing output
+    wl = WORKLOADS["biased_grouped_e256"]
+    for _ in range(calls):
+        mr.route_dispatch_metadata(ids, wl.E, w)
+    torch.cuda.synchronize()
+    eprint(f"[profile] dispatch metadata: {calls} calls")
+    # fused routers: the 7168-wide one on its default split path and as one
+    # kernel, then the few-expert ones
+    wl = WORKLOADS["fused_router_h7168"]
+    hidden, wr = make_router_inputs(wl)
+    hs = sets(dev_tensor(hidden), min(calls, 3))
+    wd, bd = dev_tensor(wr), dev_tensor(make_bias(wl))
+    for ws in (None, False):
+        for h in hs:
+            mr.route_fused_router(h, wd, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", bd,
+                                  "top2sum", workspace=ws)
+        torch.cuda.synchronize()
+        eprint(f"[profile] {wl.name} ({'split path' if ws is None else 'one kernel'})")
+    del hs
+    for name in ("fused_router_e8_h4096", "fused_router_e16_h6144"):
+        wl = WORKLOADS[name]
+        hidden, wr = make_router_inputs(wl)
+        hs = sets(dev_tensor(hidden), min(calls, 3))
+        wd = dev_tensor(wr)
+        for h in hs:
+            mr.route_fused_router(h, wd, wl.K, 1, 1, wl.renormalize, wl.scoring, None, "max",
+                                  logit_softcap=wl.softcap)
+        torch.cuda.synchronize()
+        eprint(f"[profile] {name}")
+        del hs
+    print(json.dumps({"profile_run": "done", "calls": calls}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,6 +529,8 @@ def main():
     ap.add_argument("--all-out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM byte counter scaling)")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only run a few calls of every workload (for rocprofv3 passes)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -467,6 +539,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.profile_run:
+        profile_run()
         return
 
     import numpy as np
