@@ -292,23 +292,20 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
             L[m * kFrE + n] = cap != 0.0f ? cap * tanh_f32(acc[0][nt][j] / cap) : acc[0][nt][j];
         }
     }
-    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias_at(bias, t);
+    // key window (every routing wave), and the staged bias offsets: wave i
+    // writes entries [64 i, 64 i + 64)
+    KeyParams kp = key_params(0.0f, 1.0f);
+    if constexpr (BIAS) {
+        if (!copier) {
+            float b[4];
+            kp = bias_key_params<kFrE>(bias, b);
+            if (t < kFrE) s_bias[bias_elem<kFrE>(t)] = sel_offset(b[t / kWave], kp);
+        }
+    }
     __syncthreads();
     if (copier) return;
 
     const int r = t / 8, sub = t % 8, rw_in_wave = (t % kWave) / 8;
-    KeyParams kp;
-    if constexpr (BIAS) {
-        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            bmin = fminf(bmin, s_bias[sub * 32 + j]);
-            bmax = fmaxf(bmax, s_bias[sub * 32 + j]);
-        }
-        kp = key_params(row_min<8>(bmin), 1.0f + row_max<8>(bmax));
-    } else {
-        kp = key_params(0.0f, 1.0f);
-    }
     float x[32];
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -470,7 +467,16 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
         a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
     }
     red[q][c4] = a;
-    if (BIAS && t < kFrE) s_bias[bias_elem<kFrE>(t)] = bias_at(bias, t);
+    // key window (waves 0-3, which stage the bias offsets: wave i entries
+    // [64 i, 64 i + 64); wave 0 routes the row)
+    KeyParams kp = key_params(0.0f, 1.0f);
+    if constexpr (BIAS) {
+        if (t < kFrE) {
+            float b[4];
+            kp = bias_key_params<kFrE>(bias, b);
+            s_bias[bias_elem<kFrE>(t)] = sel_offset(b[t / kWave], kp);
+        }
+    }
     __syncthreads();
     if (q == 0) {
 #pragma unroll
@@ -490,18 +496,6 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     if (t >= kWave) return;
 
     const int sub = t % 8, rw = t / 8;
-    KeyParams kp;
-    if constexpr (BIAS) {
-        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            bmin = fminf(bmin, s_bias[sub * 32 + j]);
-            bmax = fmaxf(bmax, s_bias[sub * 32 + j]);
-        }
-        kp = key_params(row_min<8>(bmin), 1.0f + row_max<8>(bmax));
-    } else {
-        kp = key_params(0.0f, 1.0f);
-    }
     float x[32];
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
@@ -528,9 +522,13 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     const int t = threadIdx.x, sub = t % 8, rw = t / 8;
     const int64_t row = (int64_t)blockIdx.x * 8 + rw;
     const int64_t rrow = row < M ? row : M - 1;
+    // key window, and the staged bias offsets (lane l: entries l + 64 i)
+    KeyParams kp = key_params(0.0f, 1.0f);
     if constexpr (BIAS) {
+        float b[4];
+        kp = bias_key_params<kFrE>(bias, b);
 #pragma unroll
-        for (int i = t; i < kFrE; i += kWave) s_bias[bias_elem<kFrE>(i)] = bias_at(bias, i);
+        for (int i = 0; i < 4; ++i) s_bias[bias_elem<kFrE>(t + kWave * i)] = sel_offset(b[i], kp);
     }
     const int64_t split_stride = M * kFrE;
     const float* src = part + rrow * kFrE + sub * 32;
@@ -554,18 +552,6 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     }
     __syncthreads();
 
-    KeyParams kp;
-    if constexpr (BIAS) {
-        float bmin = INFINITY, bmax = -INFINITY;  // the layout keeps each lane's 32 together
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            bmin = fminf(bmin, s_bias[sub * 32 + j]);
-            bmax = fmaxf(bmax, s_bias[sub * 32 + j]);
-        }
-        kp = key_params(row_min<8>(bmin), 1.0f + row_max<8>(bmax));
-    } else {
-        kp = key_params(0.0f, 1.0f);
-    }
     // the logit of expert e, summed in the same order (route_rows reads it only
     // with one lane per row, so not here; it stays exact for any later use)
     const float* rsrc = part + rrow * kFrE;

@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
     static_assert(GRP == 0 || LPR == 8, "grouped kernels hold one of 8 groups per lane");
 
-    // Unbiased scores of the wave's rows (the candidate exchange and the
-    // weights read them); the block's bias.
+    // Selection scores of the wave's rows (the candidate exchange and the
+    // weights read them); the block's staged bias offsets.
     constexpr int ROW = LPR > 1 ? E : 4;  // fp32 values per row in LDS
     __shared__ __align__(16) float s_s[kWavesPerBlock][RPW * ROW];
     __shared__ __align__(16) float s_bias[BIAS ? E : 4];
@@ -140,8 +140,11 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
     if constexpr (BIAS) {
         const float bmin = has_b ? fminf(fminf(bq.x, bq.y), fminf(bq.z, bq.w)) : INFINITY;
         const float bmax = has_b ? fmaxf(fmaxf(bq.x, bq.y), fmaxf(bq.z, bq.w)) : -INFINITY;
-        if (wv == 0 && has_b) *reinterpret_cast<float4*>(s_bias + bias_chunk<E>(lane) * 4) = bq;
         kp = key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
+        if (wv == 0 && has_b)
+            *reinterpret_cast<float4*>(s_bias + bias_chunk<E>(lane) * 4) =
+                make_float4(sel_offset(bq.x, kp), sel_offset(bq.y, kp), sel_offset(bq.z, kp),
+                            sel_offset(bq.w, kp));
         __syncthreads();
     } else {
         kp = key_params(0.0f, 1.0f);

@@ -137,6 +137,11 @@ __device__ __forceinline__ int swz_elem(int e) { return swz_chunk(e >> 2) * 4 + 
 struct KeyParams {
     float scale, offs;
     bool exact_only;  // the fixed-point step would be too coarse
+    // With a correction bias the routing core holds y = fma(s, sel_mul,
+    // off[e]) per expert, where off[e] is the staged offset of the expert's
+    // bias (sel_offset): the fixed-point value t of c = s + bias on the key
+    // path, c itself on the exact path.  sel_inv = 1 / sel_mul (a power of 2).
+    float sel_mul, sel_inv;
 };
 
 // Choose the fixed-point window [lo, lo + R) that holds every selection score.
@@ -149,7 +154,33 @@ __device__ __forceinline__ KeyParams key_params(float cmin, float cmax) {
     kp.scale = 8388608.0f / R;
     kp.offs = 8388608.0f - lo * kp.scale;
     kp.exact_only = R > 4.0f;
+    kp.sel_mul = kp.exact_only ? 1.0f : kp.scale;
+    kp.sel_inv = kp.exact_only ? 1.0f : R * (1.0f / 8388608.0f);
     return kp;
+}
+
+// The staged offset of a bias value: its fixed-point image b * scale + offs
+// (an integer in [2^23, 2^24)), so that one fma of the score gives the
+// fixed-point value of c = s + b within one step; on the exact path, b.
+__device__ __forceinline__ float sel_offset(float b, const KeyParams& kp) {
+    return kp.exact_only ? b : __builtin_fmaf(b, kp.scale, kp.offs);
+}
+
+// Key window of a biased routing call, computed by every lane of a full
+// wave: lane l reads the bias entries l, l + 64, l + 128, l + 192 (those
+// below E) into b[]; the range is reduced over the wave.
+template <int E>
+__device__ __forceinline__ KeyParams bias_key_params(const BiasRef& bias, float (&b)[4]) {
+    static_assert(E <= 4 * kWave, "four bias entries per lane");
+    const int lane = threadIdx.x % kWave;
+    float bmin = INFINITY, bmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + kWave * i;
+        b[i] = e < E ? bias_at(bias, e) : 0.0f;
+        if (e < E) { bmin = fminf(bmin, b[i]); bmax = fmaxf(bmax, b[i]); }
+    }
+    return key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
 }
 
 // Offsets inside a row of the per-wave LDS tile (ROW fp32 values); 16-byte
@@ -186,8 +217,8 @@ __device__ __forceinline__ float lane_score(float x, float mx) {
 // Route the rows of one wave tile.  Lane `sub` of row-in-wave `rw` brings the
 // fp32 logits x[0..VPL) of experts [sub*VPL, sub*VPL + VPL) of token `row`
 // (valid == false past the last token: computed, never stored).  my_row is
-// this row's E-float LDS scratch (LPR > 1); s_bias the bias in LDS, in the
-// bias_elem layout (BIAS);
+// this row's E-float LDS scratch (LPR > 1); s_bias the staged bias offsets
+// (sel_offset of each expert's bias) in LDS, in the bias_elem layout (BIAS);
 // logit_of(e) returns the fp32 logit of expert e of this row (rare paths).
 // Steps follow "[SGLang] MoE routing: token-to-expert assignment algorithms",
 // sections 2-4; see the file header of route_fast.hip for the design.
@@ -235,10 +266,16 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         if constexpr (SOFTMAX) row_total = row_sum<LPR>(acc);
     }
     if constexpr (BIAS) {
+        // y = fma(s, sel_mul, offset): the fixed-point value t of c = s + bias
+        // (or c itself on the exact path)
+        const float a = kp.sel_mul;
 #pragma unroll
         for (int v = 0; v < CPL; ++v) {
             const float4 d = reinterpret_cast<const float4*>(s_bias)[bias_chunk<E>(sub * CPL + v)];
-            x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
+            x[4 * v] = __builtin_fmaf(x[4 * v], a, d.x);
+            x[4 * v + 1] = __builtin_fmaf(x[4 * v + 1], a, d.y);
+            x[4 * v + 2] = __builtin_fmaf(x[4 * v + 2], a, d.z);
+            x[4 * v + 3] = __builtin_fmaf(x[4 * v + 3], a, d.w);
         }
     }
     if constexpr (LPR > 1) {
@@ -247,19 +284,30 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
             reinterpret_cast<float4*>(my_row)[tile_chunk<ROW>(sub * CPL + v, rw)] =
                 make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
     }
-    // x now holds the selection scores c of the lane's experts
+    // x now holds the selection scores c of the lane's experts, or with a
+    // bias (key path) their fixed-point values t in [2^23, 2^24)
 
     // ---- 2. group score, rank among the row's 8 groups, keep the best TG
     uint32_t kept_row = 1u;
     if constexpr (GRP != 0) {
+        // top two of the lane's values, two values a step: the new second is
+        // the larger of the old second and the median of (m1, a, b)
         float m1 = -INFINITY, m2 = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            if (GRP == 2) m2 = __builtin_amdgcn_fmed3f(m1, m2, x[j]);
-            m1 = fmaxf(m1, x[j]);
+        for (int j = 0; j < VPL; j += 2) {
+            if (GRP == 2) m2 = fmaxf(__builtin_amdgcn_fmed3f(m1, x[j], x[j + 1]), m2);
+            m1 = fmaxf(fmaxf(m1, x[j]), x[j + 1]);
         }
-        const float h = GRP == 2 ? m1 + m2 : m1;
-        const uint32_t hq = static_cast<uint32_t>(__builtin_fmaf(h, kp.scale, h_offs));
+        uint32_t hq;
+        if constexpr (BIAS) {
+            // t values are integers below 2^24 in fp32: their bits less the
+            // exponent field are the fixed-point values, summed exactly
+            hq = GRP == 2 ? __float_as_uint(m1) + __float_as_uint(m2) - 2u * 0x4B000000u
+                          : __float_as_uint(m1) - 0x4B000000u;
+        } else {
+            const float h = GRP == 2 ? m1 + m2 : m1;
+            hq = static_cast<uint32_t>(__builtin_fmaf(h, kp.scale, h_offs));
+        }
         const uint32_t hk = (hq << 3) | static_cast<uint32_t>(7 - sub);
         uint32_t rank = 0;
         const uint32_t m7 = dpp_u32<kDppMirror8>(hk);
@@ -321,8 +369,11 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         if (has_cand) {
 #pragma unroll
             for (int j = 0; j < NC; ++j)
-                list_insert<T, TR>(L, make_key(cc[j], kp.scale, kp.offs, (uint32_t)(NC - 1 - j)),
-                                   ev);
+                list_insert<T, TR>(
+                    L,
+                    BIAS ? (__float_as_uint(cc[j]) << 9) | (uint32_t)(NC - 1 - j)
+                         : make_key(cc[j], kp.scale, kp.offs, (uint32_t)(NC - 1 - j)),
+                    ev);
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) L[t] += base9;
@@ -455,10 +506,12 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         pick[s] = min(max(pick[s], 0), E - 1);  // never read outside the row
         float sv;
         if constexpr (LPR > 1) {
-            // the row holds c; the weight is the unbiased score c - bias
-            // (within a few fp32 ulps of s)
+            // the row holds c, or with a bias fma(s, sel_mul, offset): the
+            // weight is the unbiased score, (y - offset) / sel_mul (exact
+            // subtraction; s to within half a key step, or c - bias on the
+            // exact path)
             sv = my_row[tile_elem<ROW>(pick[s], rw)];
-            if constexpr (BIAS) sv -= s_bias[bias_elem<E>(pick[s])];
+            if constexpr (BIAS) sv = (sv - s_bias[bias_elem<E>(pick[s])]) * kp.sel_inv;
         } else if constexpr (SOFTMAX) {
             sv = x[0];  // one lane per row: x holds the numerators
 #pragma unroll
