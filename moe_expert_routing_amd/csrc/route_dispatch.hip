@@ -8,8 +8,16 @@
 // (gather), the sorted position of each assignment (scatter), and the
 // weights in sorted order.  Ids outside [0, E) are dropped.
 //
-// Three kernels, all on the caller's stream, with a caller-provided
-// workspace cnt[B][E] + totals[E] (B = blocks of kBlockChunk assignments):
+// Up to 16384 counts in a coarse matrix (the usual case: 65536 tokens x 8
+// slots over 256 experts), two kernels on the caller's stream:
+//   1. hist:  one count row per 8192 assignments, cnt[C][E];
+//   2. place: as in 3. below, except that each block first reduces the whole
+//             coarse matrix itself (its rows before the block's own row give
+//             the counts of earlier blocks, all rows the expert totals) and
+//             recounts the at most three 2048-assignment chunks of its own
+//             row that precede it.
+// Otherwise three kernels, with a caller-provided workspace cnt[B][E] +
+// totals[E] (B = blocks of kBlockChunk assignments):
 //   1. hist:  each block counts its chunk per expert (LDS atomics) into its
 //             row cnt[b][*];
 //   2. scan:  64 experts per block, each column cnt[*][e] split over 16
@@ -27,6 +35,7 @@
 //             atomics.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "route_common.hpp"
@@ -51,26 +60,39 @@ constexpr int kBlockChunk = kDispWaves * kWaveChunk;     // 2048 per block
 constexpr int kScanThreads = 1024;                       // >= max experts
 constexpr int kScanBatch = 16;                           // loads in flight per thread
 
+// Coarse counts: one row per kCoarseChunk assignments, read whole by every
+// place block when the matrix holds at most kCoarseMaxInts counts.
+constexpr int kCoarseThreads = 1024;
+constexpr int kCoarsePer = 8;                                    // assignments per thread
+constexpr int kCoarseChunk = kCoarseThreads * kCoarsePer;        // 8192 per row
+constexpr int kSubPerRow = kCoarseChunk / kBlockChunk;           // 4 place blocks per row
+constexpr int kCoarseMaxInts = 16384;                            // 64 KiB
+constexpr int kCoarseRowsPerLane = kCoarseMaxInts / 4 / kDispThreads;  // int4 loads, <= 8
+static_assert(kCoarseChunk % kBlockChunk == 0, "place blocks tile a coarse row");
+
 __device__ __forceinline__ bool valid_id(int32_t id, int E) { return id >= 0 && id < E; }
 
-__global__ __launch_bounds__(kDispThreads) void dispatch_hist_kernel(
+// Block b counts assignments [b * THREADS * PER, +THREADS * PER) per expert
+// (LDS atomics) into row cnt[b][*].
+template <int THREADS, int PER>
+__global__ __launch_bounds__(THREADS) void dispatch_hist_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ cnt) {
     extern __shared__ int32_t s_hist[];  // [E]
     const int t = threadIdx.x;
-    const int64_t a0 = (int64_t)blockIdx.x * kBlockChunk + t;
-    int32_t idv[kPerLane];  // all loads in flight at once
+    const int64_t a0 = (int64_t)blockIdx.x * (THREADS * PER) + t;
+    int32_t idv[PER];  // all loads in flight at once
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-        const int64_t a = a0 + (int64_t)j * kDispThreads;
+    for (int j = 0; j < PER; ++j) {
+        const int64_t a = a0 + (int64_t)j * THREADS;
         idv[j] = a < n ? ids[a] : -1;
     }
-    for (int e = t; e < E; e += kDispThreads) s_hist[e] = 0;
+    for (int e = t; e < E; e += THREADS) s_hist[e] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
+    for (int j = 0; j < PER; ++j)
         if (valid_id(idv[j], E)) atomicAdd(&s_hist[idv[j]], 1);
     __syncthreads();
-    for (int e = t; e < E; e += kDispThreads) cnt[(int64_t)blockIdx.x * E + e] = s_hist[e];
+    for (int e = t; e < E; e += THREADS) cnt[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
 // Block x, thread t: expert e = 64 x + t % 64 over segment t / 64 of the
@@ -137,22 +159,32 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     }
 }
 
+// LDS layout of the place kernel: offsets [E + 1], carries [kDispWaves], then
+// (16-byte aligned) the per-wave counts and cursors, or first the coarse
+// partials.
+__host__ __device__ constexpr int place_cur_offset(int E) { return (E + 1 + kDispWaves + 3) & ~3; }
+
+// COARSE: cnt is the coarse matrix [C][E] (E a multiple of 4, 16-byte
+// aligned rows, C * E <= kCoarseMaxInts) and totals is unused; otherwise cnt
+// holds the scanned rows [B][E] and totals the expert totals.
+template <bool COARSE>
 __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t n, int E,
-    const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ totals, int C,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ gather,
     int32_t* __restrict__ scatter, float* __restrict__ sorted_w) {
     extern __shared__ int32_t smem[];
     int32_t* s_off = smem;                     // [E + 1] expert offsets
     int32_t* s_wsum = s_off + E + 1;           // [kDispWaves] scan carries
-    int32_t* s_cur = s_wsum + kDispWaves;      // [kDispWaves][E] counts, then cursors
+    int32_t* s_cur = smem + place_cur_offset(E);  // [kDispWaves][E] counts, then cursors
     constexpr int kEPT = kMaxExperts / kDispThreads;  // experts per thread (<= 4)
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wv = t / kWave;
     // every global load of the block goes out first: this lane's assignments
     // a0 + 64 j, the expert totals (experts kEPT t ..), the block's row of
-    // offsets across blocks
+    // offsets across blocks (COARSE: the coarse matrix and the assignments
+    // to recount)
     const int64_t a0 = (int64_t)blockIdx.x * kBlockChunk + (int64_t)wv * kWaveChunk + lane;
     int32_t idv[kPerLane];
     float wv8[kPerLane];
@@ -162,13 +194,78 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         idv[j] = a < n ? ids[a] : -1;
         wv8[j] = (sorted_w && a < n) ? wts[a] : 0.0f;
     }
-    const int32_t* row = cnt + (int64_t)blockIdx.x * E;
     int tot[kEPT], rowv[kEPT];
+    if constexpr (COARSE) {
+        // Thread t < Q * G reduces 16-byte quad q = t % Q of rows
+        // r = g, g + G, ... (g = t / Q) into a before-my-row and an all-rows
+        // partial; the G partials of an expert are added in LDS.  The
+        // assignments of the preceding chunks of this block's coarse row are
+        // recounted into s_cur row 0.
+        const int Q = E / 4, G = kDispThreads / Q;
+        const int c = blockIdx.x / kSubPerRow;
+        const int q = t % Q, g = t / Q;
+        int4 m[kCoarseRowsPerLane];
 #pragma unroll
-    for (int i = 0; i < kEPT; ++i) {
-        const int e = kEPT * t + i;
-        tot[i] = e < E ? totals[e] : 0;
-        rowv[i] = e < E ? row[e] : 0;
+        for (int i = 0; i < kCoarseRowsPerLane; ++i) {
+            const int r = g + G * i;
+            m[i] = (g < G && r < C)
+                       ? reinterpret_cast<const int4*>(cnt + (int64_t)r * E)[q]
+                       : make_int4(0, 0, 0, 0);
+        }
+        const int64_t rc0 = (int64_t)c * kCoarseChunk;
+        const int nrc = (blockIdx.x % kSubPerRow) * kBlockChunk;  // assignments to recount
+        int32_t rid[kSubPerRow - 1][kPerLane];
+#pragma unroll
+        for (int u = 0; u < kSubPerRow - 1; ++u)
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) {
+                const int o = (u * kPerLane + j) * kDispThreads + t;
+                rid[u][j] = o < nrc ? ids[rc0 + o] : -1;  // rc0 + o < n: earlier chunks are full
+            }
+        int32_t* s_pre = s_cur;                    // [G][E] partials (rows before c)
+        int32_t* s_all = s_cur + G * E;            // [G][E] partials (all rows)
+        int32_t* s_rc = s_all + G * E;             // [E] recount
+        for (int e = t; e < E; e += kDispThreads) s_rc[e] = 0;
+        if (g < G) {
+            int4 pre = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < kCoarseRowsPerLane; ++i) {
+                all.x += m[i].x; all.y += m[i].y; all.z += m[i].z; all.w += m[i].w;
+                if (g + G * i < c) { pre.x += m[i].x; pre.y += m[i].y; pre.z += m[i].z; pre.w += m[i].w; }
+            }
+            reinterpret_cast<int4*>(s_pre + g * E)[q] = pre;
+            reinterpret_cast<int4*>(s_all + g * E)[q] = all;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kSubPerRow - 1; ++u)
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j)
+                if (valid_id(rid[u][j], E)) atomicAdd(&s_rc[rid[u][j]], 1);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kEPT; ++i) {
+            const int e = kEPT * t + i;
+            int p = 0, a = 0;
+            if (e < E) {
+                for (int gg = 0; gg < G; ++gg) {
+                    p += s_pre[gg * E + e];
+                    a += s_all[gg * E + e];
+                }
+                p += s_rc[e];
+            }
+            tot[i] = a;
+            rowv[i] = p;
+        }
+        __syncthreads();  // s_cur is reused below
+    } else {
+        const int32_t* row = cnt + (int64_t)blockIdx.x * E;
+#pragma unroll
+        for (int i = 0; i < kEPT; ++i) {
+            const int e = kEPT * t + i;
+            tot[i] = e < E ? totals[e] : 0;
+            rowv[i] = e < E ? row[e] : 0;
+        }
     }
     // expert offsets: exclusive scan of the totals over the block
     int sum = 0;
@@ -290,18 +387,39 @@ size_t dispatch_workspace_bytes(int64_t n, int E) {
 route_status_t launch_dispatch(const DispatchProblem& d) {
     const int B = static_cast<int>((d.n + kBlockChunk - 1) / kBlockChunk);
     int32_t* cnt = static_cast<int32_t*>(d.workspace);
-    int32_t* totals = cnt + static_cast<int64_t>(d.E) * B;
     static_assert(kMaxExperts % kDispThreads == 0, "experts per place thread");
+    const int C = static_cast<int>((d.n + kCoarseChunk - 1) / kCoarseChunk);
+    // coarse partial groups of the place kernel: G threads per 16-byte quad,
+    // each reducing up to kCoarseRowsPerLane rows
+    const int G = d.E >= 4 ? kDispThreads / (d.E / 4) : 0;
+    const bool coarse = B > 0 && d.E % 4 == 0 && (int64_t)C * d.E <= kCoarseMaxInts &&
+                        C <= kCoarseRowsPerLane * G &&
+                        (reinterpret_cast<uintptr_t>(cnt) & 15u) == 0;
+    if (coarse) {
+        // place LDS: offsets, carries, and the larger of the per-wave counts
+        // and the coarse partials (2 G E + E)
+        const size_t cur_ints = std::max<size_t>((size_t)kDispWaves * d.E, (size_t)(2 * G + 1) * d.E);
+        hipLaunchKernelGGL((dispatch_hist_kernel<kCoarseThreads, kCoarsePer>), dim3(C),
+                           dim3(kCoarseThreads), sizeof(int32_t) * d.E, d.stream, d.ids, d.n,
+                           d.E, cnt);
+        hipLaunchKernelGGL(dispatch_place_kernel<true>, dim3(B), dim3(kDispThreads),
+                           sizeof(int32_t) * (place_cur_offset(d.E) + cur_ints), d.stream, d.ids,
+                           d.weights, d.n, d.E, cnt, nullptr, C, d.counts, d.offsets, d.gather,
+                           d.scatter, d.sorted_weights);
+        return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
+    }
+    int32_t* totals = cnt + static_cast<int64_t>(d.E) * B;
     if (B > 0) {
-        hipLaunchKernelGGL(dispatch_hist_kernel, dim3(B), dim3(kDispThreads),
-                           sizeof(int32_t) * d.E, d.stream, d.ids, d.n, d.E, cnt);
+        hipLaunchKernelGGL((dispatch_hist_kernel<kDispThreads, kPerLane>), dim3(B),
+                           dim3(kDispThreads), sizeof(int32_t) * d.E, d.stream, d.ids, d.n, d.E,
+                           cnt);
     }
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3((d.E + kWave - 1) / kWave), dim3(kScanThreads),
                        0, d.stream, d.E, B, cnt, totals);
-    hipLaunchKernelGGL(dispatch_place_kernel, dim3(B > 0 ? B : 1), dim3(kDispThreads),
-                       sizeof(int32_t) * (d.E + 1 + kDispWaves + kDispWaves * d.E), d.stream,
-                       d.ids, d.weights, d.n, d.E, cnt, totals, d.counts, d.offsets, d.gather,
-                       d.scatter, d.sorted_weights);
+    hipLaunchKernelGGL(dispatch_place_kernel<false>, dim3(B > 0 ? B : 1), dim3(kDispThreads),
+                       sizeof(int32_t) * (place_cur_offset(d.E) + kDispWaves * d.E), d.stream,
+                       d.ids, d.weights, d.n, d.E, cnt, totals, B, d.counts, d.offsets,
+                       d.gather, d.scatter, d.sorted_weights);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 

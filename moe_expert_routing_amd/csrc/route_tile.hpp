@@ -20,6 +20,15 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return static_cast<uint32_t>(
         __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
+// A plain DPP move for values that are compared rather than combined (the
+// form above folds into the combining instruction; this one needs no zeroed
+// old value).  Every control used here (quad_perm, row_half_mirror) reads a
+// lane of the same row for every lane, so no lane keeps an old value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u32(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
@@ -310,14 +319,14 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         }
         const uint32_t hk = (hq << 3) | static_cast<uint32_t>(7 - sub);
         uint32_t rank = 0;
-        const uint32_t m7 = dpp_u32<kDppMirror8>(hk);
-        rank += dpp_u32<kDppXor1>(hk) > hk;
-        rank += dpp_u32<kDppXor2>(hk) > hk;
-        rank += dpp_u32<kDppXor3>(hk) > hk;
+        const uint32_t m7 = dpp_mov_u32<kDppMirror8>(hk);
+        rank += dpp_mov_u32<kDppXor1>(hk) > hk;
+        rank += dpp_mov_u32<kDppXor2>(hk) > hk;
+        rank += dpp_mov_u32<kDppXor3>(hk) > hk;
         rank += m7 > hk;
-        rank += dpp_u32<kDppXor1>(m7) > hk;
-        rank += dpp_u32<kDppXor2>(m7) > hk;
-        rank += dpp_u32<kDppXor3>(m7) > hk;
+        rank += dpp_mov_u32<kDppXor1>(m7) > hk;
+        rank += dpp_mov_u32<kDppXor2>(m7) > hk;
+        rank += dpp_mov_u32<kDppXor3>(m7) > hk;
         const uint64_t kept_wave = __ballot(rank < static_cast<uint32_t>(TG));
         kept_row = static_cast<uint32_t>(kept_wave >> (rw * LPR)) & 0xffu;
     }

@@ -37,6 +37,9 @@ def _compare(ids_np, E, w_np=None, workspace=None):
     (513, 1, 1024, -5, 1024, 5), # widest expert id (11 bits)
     (20000, 2, 1, -1, 1, 6),     # one expert, half the ids dropped
     (70001, 8, 256, -2, 258, 7), # 274 blocks: the scan reads its columns in two batches
+    (98000, 8, 160, 0, 160, 8),  # two kernels: 96 coarse rows, every reducing thread's last
+    (40000, 8, 384, -1, 385, 10),  # two kernels: 40 coarse rows over 5 reducing groups
+    (65536, 8, 252, 0, 252, 11), # two kernels: 64 coarse rows of 63 quads (not a power of 2)
 ])
 def test_dispatch_random_ids(M, K, E, lo, hi, seed):
     rng = np.random.default_rng(seed)
