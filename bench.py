@@ -411,7 +411,8 @@ def measure_all(out_path=None):
     r = {"workload": "dispatch_metadata_e256_m65536", "entry": "route_dispatch_metadata",
          "M": wl.M, "K": wl.K, "E": wl.E, "rotating_sets": n_sets, "us_per_call": per_call,
          "kernel_us": kern, "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
-         "note": "three kernels per call; us_per_call includes the library's allocations "
+         "note": "two kernels per call at this size (three when the coarse count matrix "
+                 "exceeds 16384 counts); us_per_call includes the library's allocations "
                  "of the outputs in the Python binding"}
     results.append(r)
     eprint(json.dumps(r))
@@ -704,6 +705,18 @@ def main():
         "M64": {"kernel_us_event_pairs": m64_kernel_us, "loop_us_per_call": m64_loop_us,
                 "graph_us_per_call": graph_us},
         "wall_s_timed": wall,
+    }
+    # The goals set for this workload: >= 70% of HBM peak at 65536 tokens and
+    # <= 5 us per call at 64 tokens.  The first is not met: the kernel is
+    # bound by VALU issue (about 570 instructions per 8-row tile), not by
+    # HBM bytes (its traffic is 1.007x the algorithmic bytes).
+    frac = achieved / HBM_PEAK_GBPS
+    result["targets"] = {
+        "hbm_frac": {"target": 0.70, "measured": frac, "met": frac >= 0.70,
+                     "note": "not met: VALU-issue bound, traffic 1.007x algorithmic"
+                     if frac < 0.70 else "met"},
+        "m64_us": {"target": 5.0, "measured_graph": graph_us,
+                   "met": graph_us is not None and graph_us <= 5.0},
     }
     if args.all_configs:
         measure_all(args.all_out)
