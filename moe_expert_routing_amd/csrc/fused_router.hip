@@ -316,7 +316,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const float* lrow = L + r * kFrE;
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
         x, sub, rw_in_wave, row < M, row, S + r * kFrE, s_bias, kp, TG, K, renorm, w_out,
-        id_out, [&](int e) { return lrow[e]; });
+        id_out, [&](int e) { return lrow[e]; },
+        [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
 }
 
 // ---- up to 8192 tokens: the hidden dimension split over workgroups
@@ -504,7 +505,8 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     }
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
         x, sub, rw, rw == 0, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
-        [&](int e) { return L[e]; });
+        [&](int e) { return L[e]; },
+        [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
 }
 
 // Otherwise a wave per 8 rows, in the routing kernel's layout: lane sub of
@@ -561,7 +563,8 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
             float v = rsrc[e];
             for (int sp = 1; sp < nsplit; ++sp) v += rsrc[sp * split_stride + e];
             return cap != 0.0f ? cap * tanh_f32(v / cap) : v;
-        });
+        },
+        [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
 }
 
 template <bool SOFTMAX, bool BIAS, int GRP>

@@ -40,6 +40,36 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
     return fast_rcp(1.0f + fast_exp2(x * -kLog2e));
 }
 
+// e^v in double precision, for the rare re-ranking of near-tied picks (a
+// relative error near 1e-14 is far more than that needs): Cody and Waite's
+// reduction v = n ln2 + r (ln2 split into its nearest float, so that n * hi
+// is exact, and the float nearest the remainder), then e^r = (e^(r/64))^64
+// with the Taylor series of e^(r/64) to degree 6.  With |r/64| below 0.017
+// every coefficient can be a float value (its rounding, times (r/64)^3 or
+// smaller, stays below 1e-13), so all constants are 32-bit literals and no
+// register holds a 64-bit constant.  Arguments are clamped to the range
+// where e^v is finite and normal.
+__device__ __forceinline__ double exp_f64(double v) {
+    v = fmin(fmax(v, -708.0), 709.0);
+    const double n = rint(v * (double)1.44269502f);  // ~1/ln2; n may be off by one
+    const double r = fma(-n, (double)-1.90465421e-09f,  // ~ln2 - hi
+                         fma(-n, (double)0.693147182f, v));  // hi: float nearest ln2
+    const double q = r * 0.015625;  // r / 64, exact
+    double p = (double)(1.0f / 720.0f);
+    p = fma(p, q, (double)(1.0f / 120.0f));
+    p = fma(p, q, (double)(1.0f / 24.0f));
+    p = fma(p, q, (double)(1.0f / 6.0f));
+    p = fma(p, q, 0.5);
+    p = fma(p, q, 1.0);
+    p = fma(p, q, 1.0);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) p *= p;
+    return ldexp(p, static_cast<int>(n));
+}
+
+// sigmoid in double precision: 1 / (1 + e^-x), correctly rounded division.
+__device__ __forceinline__ double sigmoid_f64(double x) { return 1.0 / (1.0 + exp_f64(-x)); }
+
 // tanh(y) = sign(y) * (1 - 2 / (exp(2|y|) + 1)); absolute error ~1e-7, and
 // exactly +-1 once exp overflows.
 __device__ __forceinline__ float tanh_f32(float y) {

@@ -90,7 +90,7 @@ struct RawLane<float, VPL> {
 
 template <typename T, int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/,
           int SPLIT, int TL, int KMAX>
-__global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
+__global__ __launch_bounds__(kWavesPerBlock* kWave, 3) void route_fast_kernel(
     const T* __restrict__ logits, BiasRef bias, int64_t M, int TG, int K, int renorm,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     constexpr int E = LPR * VPL;
@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave) void route_fast_kernel(
         const T* xr = logits + (valid ? row : 0) * E;
         route_rows<LPR, VPL, SOFTMAX, BIAS, GRP, SPLIT, TL, KMAX>(
             x, sub, rw, valid, row, my_row, s_bias, kp, TG, K, renorm, w_out, id_out,
-            [&](int e) { return load_one<T>(xr, e); });
+            [&](int e) { return load_one<T>(xr, e); },
+            [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
     };
     // The second tile is requested only once the first has arrived: at the
     // start every wave of the grid requests at once, and second tiles

@@ -14,6 +14,7 @@ constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppXor3 = 0x1B;     // quad_perm [3,2,1,0]
 constexpr int kDppMirror8 = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
 constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <-> 15 - i within 16
+constexpr int kDppRowShl1 = 0x101;    // row_shl:1: lane i reads lane i + 1 within 16
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -228,16 +229,18 @@ __device__ __forceinline__ float lane_score(float x, float mx) {
 // (valid == false past the last token: computed, never stored).  my_row is
 // this row's E-float LDS scratch (LPR > 1); s_bias the staged bias offsets
 // (sel_offset of each expert's bias) in LDS, in the bias_elem layout (BIAS);
-// logit_of(e) returns the fp32 logit of expert e of this row (rare paths).
+// logit_of(e) returns the fp32 logit of expert e of this row and bias_of(e)
+// its correction bias (0 without one) (rare paths).
 // Steps follow "[SGLang] MoE routing: token-to-expert assignment algorithms",
 // sections 2-4; see the file header of route_fast.hip for the design.
 template <int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/, int SPLIT,
-          int TL, int KMAX, typename LogitFn>
+          int TL, int KMAX, typename LogitFn, typename BiasFn>
 __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const int rw,
                                            const bool valid, const int64_t row, float* my_row,
                                            const float* s_bias, const KeyParams& kp, const int TG,
                                            const int K, const int renorm, float* __restrict__ w_out,
-                                           int32_t* __restrict__ id_out, LogitFn logit_of) {
+                                           int32_t* __restrict__ id_out, LogitFn logit_of,
+                                           BiasFn bias_of) {
     constexpr int E = LPR * VPL;
     constexpr int NC = GRP ? VPL / SPLIT : VPL;    // candidates per lane in the list step
     constexpr int SLOTS = (KMAX + LPR - 1) / LPR;  // output slots per lane
@@ -505,6 +508,54 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
         }
     }
 
+    // ---- exact order of near-tied picks (sigmoid scoring, eight lanes per
+    // row, one pick per lane).  A key is within 1.5 key steps of the exact
+    // fixed-point value of c (half a step each for the staged bias offset,
+    // the final rounding and the fp32 sigmoid), so two adjacent picks whose
+    // keys differ by more than kNearKeySteps are in the exact order.  When a
+    // row of the wave has a closer pair, the selection scores of every
+    // row's picks are recomputed in double precision and each pick takes
+    // its rank among its row's picks (c desc, expert asc) as its output
+    // slot.  The branch is taken in about one tile in a thousand.  (Near
+    // ties at the K-th pick itself, or between kept and dropped groups, are
+    // left to the keys.)
+    int slot0 = sub;  // output slot of this lane's first pick
+    if constexpr (!SOFTMAX && LPR == 8 && SLOTS == 1) {
+        // keys are (value << 9 | index bits), sorted descending along the
+        // row's lanes: a value gap of at most kNearKeySteps makes the key
+        // difference less than (kNearKeySteps + 1) << 9 (a gap one step
+        // larger may also pass: a harmless extra re-ranking)
+        constexpr uint32_t kNearKeySteps = 4;
+        const uint32_t nxt = dpp_mov_u32<kDppRowShl1>(wk[0]);
+        const bool near = !kp.exact_only && sub + 1 < K &&
+                          wk[0] - nxt < ((kNearKeySteps + 1) << 9);
+        if (__builtin_expect(__ballot(near) != 0ull, 0)) {
+            const int p0 = min(max(pick[0], 0), E - 1);
+            const double c64 = sigmoid_f64((double)logit_of(p0)) + (double)bias_of(p0);
+            // rank among the row's K picks: the other 7 lanes of the row by
+            // the all-to-all DPP pattern of the group rank (lane i ^ 1, i ^ 2,
+            // i ^ 3, 7 - i and 7 - (i ^ 1..3)); lanes sub >= K hold no pick
+            const uint32_t lo = __double2loint(c64), hi = __double2hiint(c64);
+            const uint32_t me = static_cast<uint32_t>(p0) | (static_cast<uint32_t>(sub) << 16);
+            int rank = 0;
+            auto count = [&](uint32_t olo, uint32_t ohi, uint32_t ome) {
+                const double co = __hiloint2double((int)ohi, (int)olo);
+                const int po = (int)(ome & 0xffffu), so = (int)(ome >> 16);
+                if (so < K && (co > c64 || (co == c64 && po < p0))) ++rank;
+            };
+            count(dpp_mov_u32<kDppXor1>(lo), dpp_mov_u32<kDppXor1>(hi), dpp_mov_u32<kDppXor1>(me));
+            count(dpp_mov_u32<kDppXor2>(lo), dpp_mov_u32<kDppXor2>(hi), dpp_mov_u32<kDppXor2>(me));
+            count(dpp_mov_u32<kDppXor3>(lo), dpp_mov_u32<kDppXor3>(hi), dpp_mov_u32<kDppXor3>(me));
+            const uint32_t mlo = dpp_mov_u32<kDppMirror8>(lo), mhi = dpp_mov_u32<kDppMirror8>(hi),
+                           mme = dpp_mov_u32<kDppMirror8>(me);
+            count(mlo, mhi, mme);
+            count(dpp_mov_u32<kDppXor1>(mlo), dpp_mov_u32<kDppXor1>(mhi), dpp_mov_u32<kDppXor1>(mme));
+            count(dpp_mov_u32<kDppXor2>(mlo), dpp_mov_u32<kDppXor2>(mhi), dpp_mov_u32<kDppXor2>(mme));
+            count(dpp_mov_u32<kDppXor3>(mlo), dpp_mov_u32<kDppXor3>(mhi), dpp_mov_u32<kDppXor3>(mme));
+            if (sub < K) slot0 = rank;
+        }
+    }
+
     // ---- 5. weights from the unbiased scores, renormalisation, stores
     if constexpr (LPR > 1 && GRP == 0) wave_lds_sync();
     float wsl[SLOTS];
@@ -538,9 +589,10 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
             const int r = s * LPR + sub;
+            const int o = s == 0 ? slot0 : r;
             if (r < K) {
-                w_out[row * K + r] = renorm ? wsl[s] * inv_tot : wsl[s];
-                id_out[row * K + r] = pick[s];
+                w_out[row * K + o] = renorm ? wsl[s] * inv_tot : wsl[s];
+                id_out[row * K + o] = pick[s];
             }
         }
     }

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import moe_expert_routing_amd as mr
+import oracle
 from gpu_util import log, oracle_args, route_gpu, to_device
 from parity_check import compare
 from workloads import (BIASED_GROUPED_M_SWEEP, WORKLOADS, bf16_bits_from_f32, make_bias,
@@ -252,3 +253,35 @@ def test_bad_arguments_raise_before_launch():
         mr.route_grouped_topk(x, 8, 8, 4, True, scoring_func="tanh")
     with pytest.raises(ValueError):
         mr.route_topk_softmax(x.t(), 2)                         # not contiguous
+
+
+@pytest.mark.parametrize("logit_dtype", ["bf16", "f32"])
+def test_near_tied_picks_keep_the_exact_order(logit_dtype):
+    """Pairs of experts (2j, 2j+1) whose biases differ by 3e-8 .. 6e-7 in
+    favour of the higher index, given equal high logits in every row: their
+    selection scores are closer than the kernel's fixed-point step, so the
+    keys tie and would put the lower index first.  Every row must still come
+    out in the exact order (the strict rule: only the K-th pick may differ
+    on a near tie, as it does where a planted pair straddles it)."""
+    rng = np.random.default_rng(2024)
+    M, E, K, G, TG = 4096, 256, 8, 8, 4
+    base = (rng.standard_normal(E // 2) * 0.05).astype(np.float32)
+    gap = rng.uniform(3e-8, 6e-7, size=E // 2)
+    b = np.empty(E, np.float32)
+    b[0::2] = base
+    b[1::2] = (base.astype(np.float64) + gap).astype(np.float32)   # odd expert ahead
+    assert (b[1::2].astype(np.float64) > b[0::2]).all()
+    xf = rng.standard_normal((M, E)).astype(np.float32)
+    for r in range(M):  # two random pairs per row get equal high logits
+        for j in rng.choice(E // 2, size=2, replace=False):
+            xf[r, 2 * j] = xf[r, 2 * j + 1] = 4.0
+    x = bf16_bits_from_f32(xf) if logit_dtype == "bf16" else xf
+    log(f"[gpu] near-tied picks M={M} logits={logit_dtype}")
+    w, ids = mr.route_biased_grouped_topk(to_device(x), to_device(b), K, G, TG, True)
+    torch.cuda.synchronize()
+    rep = compare(x, w.cpu().numpy(), ids.cpu().numpy(), scoring=oracle.SIGMOID, bias=b, G=G,
+                  TG=TG, rule=oracle.GROUP_TOP2SUM, K=K, renorm=True,
+                  label=f"planted near ties M={M} logits={logit_dtype}")
+    log(f"[gpu]   {rep.summary()}")
+    # planted pairs that straddle the K-th pick are the one allowed exception
+    assert rep.strict_ok and rep.exact + rep.near_tie_k == M, rep.summary()
