@@ -47,7 +47,12 @@
  * Precision. Scores are computed in fp32 with the GPU's exp2 and reciprocal
  *           instructions.  Expert choices therefore agree with an exact
  *           computation except where two selection scores lie within a few
- *           fp32 rounding units (a few 1e-7) of each other.
+ *           fp32 rounding units (a few 1e-7) of each other.  With sigmoid
+ *           scoring, 256 or 160 experts and top_k <= 8 (the specialised
+ *           kernels and the fused router), picks that close are re-ranked
+ *           in double precision, so the order of the chosen experts is
+ *           exact; only the K-th choice itself, or the last kept group,
+ *           can then differ from an exact computation on such a near tie.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
