@@ -264,8 +264,8 @@ def measure_all(out_path=None):
         mr.route_fused_router(hs[i], wd, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", bd,
                               "top2sum", outs[i][0], outs[i][1], stream=stream,
                               workspace=ws_arg)
-    # the library's default for this shape (two hidden splits of 64-row tiles
-    # with partial logits in the workspace), then the single fused kernel
+    # the library's default for this shape (four hidden splits of 128-row
+    # tiles with partial logits in the workspace), then the single fused kernel
     per_call, kern = time_calls(launch_fr, n_sets, stream, steps=200, warmup=20)
     per_call_one, kern_one = time_calls(lambda i: launch_fr(i, False), n_sets, stream,
                                         steps=200, warmup=20)

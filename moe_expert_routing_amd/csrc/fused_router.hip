@@ -55,13 +55,14 @@ static_assert(2 * kFrRows * kFrE * 4 <= 2 * kFrWBytes, "epilogue reuses two W st
 static_assert(kFrAStages * kFrABytes + kFrWStages * kFrWBytes + kFrE * 4 <= 160 * 1024,
               "LDS of one workgroup");
 // A ring of a ROWS-row tile: 32 rows (the fused kernel, which also keeps
-// the bias in LDS) take 12 stages of 4 KiB; 64 rows (the partial kernel, no
-// bias) take 8 stages of 8 KiB, the rest of the 160 KiB beside the W ring.
+// the bias in LDS) take 12 stages of 4 KiB; 64 and 128 rows (the partial
+// kernel, no bias) take 8 stages of 8 KiB and 4 of 16 KiB, the rest of the
+// 160 KiB beside the W ring.
 template <int ROWS> struct ARing {
     static constexpr int kBytes = ROWS * kFrBK * 2;
-    static constexpr int kStages = ROWS == 32 ? 12 : 8;
+    static constexpr int kStages = ROWS == 32 ? 12 : ROWS == 64 ? 8 : 4;
     static constexpr int kAhead = kStages - 1;
-    static constexpr int kCopies = kBytes / 1024;        // 4 or 8 wave loads per step
+    static constexpr int kCopies = kBytes / 1024;        // 4, 8 or 16 wave loads per step
     static_assert(kAhead >= kFrWAhead, "hidden states run at least as far ahead as W");
     static_assert(kStages * kBytes + kFrWStages * kFrWBytes + (ROWS == 32 ? kFrE * 4 : 0) <=
                       160 * 1024,
@@ -277,6 +278,11 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
     const int64_t m0 = (int64_t)blockIdx.x * kFrRows;
     f32x16 acc[1][2];
+    // The bias entries of the key window are requested before the main loop
+    // (they arrive before its first wait, which counts loads in issue order).
+    uint32_t braw[4];
+    if constexpr (BIAS)
+        if (wv < kFrMathWaves) bias_lane_load<kFrE>(bias, braw);
     const bool copier = fr_project<kFrRows>(hidden, w, M, H, m0, 0, H / kFrBK, sA, sW, acc);
 
     // ---- epilogue: logits to LDS, then route the 32 rows (8 lanes per row)
@@ -298,7 +304,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     if constexpr (BIAS) {
         if (!copier) {
             float b[4];
-            kp = bias_key_params<kFrE>(bias, b);
+            bias_lane_widen(bias, braw, b);
+            kp = bias_lane_key_params<kFrE>(b);
             if (t < kFrE) s_bias[bias_elem<kFrE>(t)] = sel_offset(b[t / kWave], kp);
         }
     }
@@ -325,8 +332,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
 // With fewer than 256 row tiles the single kernel leaves compute units idle
 // and each workgroup walks all of H one W tile after the other; and every
 // workgroup streams all of W for its 32 tokens.  The split path gives
-// workgroup (tile, s) the hidden steps of split s only, on tiles of 32 or 64
-// tokens (64: W is streamed once per 64 tokens); it writes its fp32 partial
+// workgroup (tile, s) the hidden steps of split s only, on tiles of 32, 64 or
+// 128 tokens (W is streamed once per tile); it writes its fp32 partial
 // logits to part[s][M][256].  A second kernel sums the splits of each logit
 // in a fixed order (so results do not depend on timing), soft-caps the sum
 // and routes the row; the summed logits never reach memory.
@@ -524,28 +531,48 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     const int t = threadIdx.x, sub = t % 8, rw = t / 8;
     const int64_t row = (int64_t)blockIdx.x * 8 + rw;
     const int64_t rrow = row < M ? row : M - 1;
-    // key window, and the staged bias offsets (lane l: entries l + 64 i)
+    // Every load is issued before the first wait: the bias entries (lane l:
+    // l + 64 i), then the logits of the first 4 splits; the key window needs
+    // only the bias.  Splits are added in split order, 4 in flight at a time.
+    uint32_t braw[4];
+    if constexpr (BIAS) bias_lane_load<kFrE>(bias, braw);
+    const int64_t split_stride = M * kFrE;
+    const float4* src = reinterpret_cast<const float4*>(part + rrow * kFrE + sub * 32);
+    float4 d[4][8];
+    auto load4 = [&](int s0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sp = min(s0 + j, nsplit - 1);  // past the last split: not added
+#pragma unroll
+            for (int v = 0; v < 8; ++v) d[j][v] = src[sp * split_stride / 4 + v];
+        }
+    };
+    load4(0);
+    // key window, and the staged bias offsets
     KeyParams kp = key_params(0.0f, 1.0f);
     if constexpr (BIAS) {
         float b[4];
-        kp = bias_key_params<kFrE>(bias, b);
+        bias_lane_widen(bias, braw, b);
+        kp = bias_lane_key_params<kFrE>(b);
 #pragma unroll
         for (int i = 0; i < 4; ++i) s_bias[bias_elem<kFrE>(t + kWave * i)] = sel_offset(b[i], kp);
     }
-    const int64_t split_stride = M * kFrE;
-    const float* src = part + rrow * kFrE + sub * 32;
     float x[32];
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-        const float4 d = reinterpret_cast<const float4*>(src)[v];
-        x[4 * v] = d.x; x[4 * v + 1] = d.y; x[4 * v + 2] = d.z; x[4 * v + 3] = d.w;
+        x[4 * v] = d[0][v].x; x[4 * v + 1] = d[0][v].y;
+        x[4 * v + 2] = d[0][v].z; x[4 * v + 3] = d[0][v].w;
     }
-#pragma unroll 4
-    for (int sp = 1; sp < nsplit; ++sp) {
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        if (s0 > 0) load4(s0);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const float4 d = reinterpret_cast<const float4*>(src + sp * split_stride)[v];
-            x[4 * v] += d.x; x[4 * v + 1] += d.y; x[4 * v + 2] += d.z; x[4 * v + 3] += d.w;
+        for (int j = 0; j < 4; ++j) {
+            if ((s0 == 0 && j == 0) || s0 + j >= nsplit) continue;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                x[4 * v] += d[j][v].x; x[4 * v + 1] += d[j][v].y;
+                x[4 * v + 2] += d[j][v].z; x[4 * v + 3] += d[j][v].w;
+            }
         }
     }
     if (cap != 0.0f) {
@@ -607,7 +634,11 @@ route_status_t launch_split(const FusedProblem& f, SplitPlan plan) {
     const int nsplit = plan.splits;
     const int64_t tiles = (f.M + plan.rows - 1) / plan.rows;
     float* part = f.workspace;  // [nsplit][M][256] fp32
-    if (plan.rows == 64)
+    if (plan.rows == 128)
+        hipLaunchKernelGGL(fused_router_partial_kernel<128>, dim3((unsigned)tiles, (unsigned)nsplit),
+                           dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                           static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
+    else if (plan.rows == 64)
         hipLaunchKernelGGL(fused_router_partial_kernel<64>, dim3((unsigned)tiles, (unsigned)nsplit),
                            dim3(kFrThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
                            static_cast<const uint16_t*>(f.w), f.M, f.H, nsplit, part);
@@ -651,13 +682,15 @@ bool fused_router_supported(const FusedProblem& f) {
 
 SplitPlan fused_router_split_plan(int64_t M, int H) {
     // One workgroup fills a compute unit (its LDS), so up to 256 workgroups
-    // run in one round.  Above 2048 tokens the partial kernel takes tiles of
-    // 64 rows: each workgroup streams W once for twice the tokens.  Split as
-    // far as one round allows, then back off to the fewest splits that keep
-    // the same steps per workgroup (every split costs partial-logit
-    // traffic).  From 129 tiles on no split fits and the single fused kernel
-    // runs.
-    const int rows = M > 2048 ? 64 : 32;
+    // run in one round.  Larger tiles stream W once for more tokens: 64 rows
+    // above 2048 tokens, 128 rows above 6144 (at 8192 tokens 4 splits of 128
+    // rows take 45.5 us a call against 51.7 for 2 splits of 64; up to 6144
+    // tokens the 64-row tiles are as fast or faster).  Split as far as one
+    // round allows, then back off to the fewest splits that keep the same
+    // steps per workgroup (every split costs partial-logit traffic).  Above
+    // 8192 tokens the single fused kernel runs.
+    if (M > 8192) return {kFrRows, 1};
+    const int rows = M > 6144 ? 128 : M > 2048 ? 64 : 32;
     const int64_t tiles = (M + rows - 1) / rows;
     const int steps = H / kFrBK;
     if (M <= 0 || steps < 2) return {kFrRows, 1};

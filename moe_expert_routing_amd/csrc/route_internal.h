@@ -81,7 +81,7 @@ bool fused_router_supported(const FusedProblem& p);
 bool small_router_supported(const FusedProblem& p);  // E = 8 or 16 (fused_router_small.hip)
 route_status_t launch_small_router(const FusedProblem& p);
 struct SplitPlan {
-    int rows;    // tokens per tile of the partial kernel (32 or 64)
+    int rows;    // tokens per tile of the partial kernel (32, 64 or 128)
     int splits;  // hidden-dimension splits; 1: the single fused kernel
 };
 SplitPlan fused_router_split_plan(int64_t M, int H);

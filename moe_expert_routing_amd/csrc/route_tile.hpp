@@ -176,21 +176,47 @@ __device__ __forceinline__ float sel_offset(float b, const KeyParams& kp) {
     return kp.exact_only ? b : __builtin_fmaf(b, kp.scale, kp.offs);
 }
 
-// Key window of a biased routing call, computed by every lane of a full
-// wave: lane l reads the bias entries l, l + 64, l + 128, l + 192 (those
-// below E) into b[]; the range is reduced over the wave.
+// The bias entries lane l of a full wave holds for the key window: l, l + 64,
+// l + 128, l + 192 (0 past E), as fp32 bit patterns.  The branch on the bias
+// type holds only the loads, so that they stay in flight past it; the bf16
+// entries are widened (exactly) where the bits are first used.
 template <int E>
-__device__ __forceinline__ KeyParams bias_key_params(const BiasRef& bias, float (&b)[4]) {
+__device__ __forceinline__ void bias_lane_load(const BiasRef& bias, uint32_t (&raw)[4]) {
     static_assert(E <= 4 * kWave, "four bias entries per lane");
+    const int lane = threadIdx.x % kWave;
+    if (bias.bf16) {
+        const uint16_t* p = static_cast<const uint16_t*>(bias.p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = lane + kWave * i < E ? p[lane + kWave * i] : 0u;
+    } else {
+        const uint32_t* p = static_cast<const uint32_t*>(bias.p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = lane + kWave * i < E ? p[lane + kWave * i] : 0u;
+    }
+}
+__device__ __forceinline__ void bias_lane_widen(const BiasRef& bias, const uint32_t (&raw)[4],
+                                                float (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = __uint_as_float(bias.bf16 ? raw[i] << 16 : raw[i]);
+}
+// Key window of a biased routing call from the entries bias_lane_load gave
+// every lane of a full wave; the range is reduced over the wave.
+template <int E>
+__device__ __forceinline__ KeyParams bias_lane_key_params(const float (&b)[4]) {
     const int lane = threadIdx.x % kWave;
     float bmin = INFINITY, bmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + kWave * i;
-        b[i] = e < E ? bias_at(bias, e) : 0.0f;
-        if (e < E) { bmin = fminf(bmin, b[i]); bmax = fmaxf(bmax, b[i]); }
-    }
+    for (int i = 0; i < 4; ++i)
+        if (lane + kWave * i < E) { bmin = fminf(bmin, b[i]); bmax = fmaxf(bmax, b[i]); }
     return key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
+}
+// Both of the above.
+template <int E>
+__device__ __forceinline__ KeyParams bias_key_params(const BiasRef& bias, float (&b)[4]) {
+    uint32_t raw[4];
+    bias_lane_load<E>(bias, raw);
+    bias_lane_widen(bias, raw, b);
+    return bias_lane_key_params<E>(b);
 }
 
 // Offsets inside a row of the per-wave LDS tile (ROW fp32 values); 16-byte

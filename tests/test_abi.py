@@ -170,7 +170,7 @@ def test_fused_router_workspace_size():
     assert ws(8, 7168, 128) == 0          # outside the compiled range
     assert ws(8, 7000, 256) == 0
     assert ws(1, 64, 256) == 0            # one hidden step: nothing to split
-    assert ws(8193, 7168, 256) == 0       # 129 tiles of 64: no split fits one round
+    assert ws(8193, 7168, 256) == 0       # above 8192 tokens: the single kernel
     assert ws(65536, 7168, 256) == 0
     # fp32 partials of every split, [M][256] each.
     # Up to 2048 tokens, tiles of 32 rows.  One tile and 112 steps of 64:
@@ -186,10 +186,14 @@ def test_fused_router_workspace_size():
     assert ws(512, 7168, 256) == 4 * 256 * 512 * 16
     # above 2048 tokens, tiles of 64 rows: 43 tiles -> 5 splits of 23 steps
     assert ws(2720, 7168, 256) == 4 * 256 * 2720 * 5
-    # 64 tiles: 4 splits of 28 steps; 65 tiles: 3 of 38; 128 tiles: 2 of 56
+    # 64 tiles: 4 splits of 28 steps; 65 tiles: 3 of 38; 96 tiles: 2 of 56
     assert ws(4096, 7168, 256) == 4 * 256 * 4096 * 4
     assert ws(4097, 7168, 256) == 4 * 256 * 4097 * 3
-    assert ws(8192, 7168, 256) == 4 * 256 * 8192 * 2
+    assert ws(6144, 7168, 256) == 4 * 256 * 6144 * 2
+    # above 6144 tokens, tiles of 128 rows: 49 tiles -> 5 splits of 23 steps;
+    # 64 tiles -> 4 of 28
+    assert ws(6145, 7168, 256) == 4 * 256 * 6145 * 5
+    assert ws(8192, 7168, 256) == 4 * 256 * 8192 * 4
 
 
 def test_binding_has_no_cpu_fallback():

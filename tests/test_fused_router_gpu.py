@@ -175,17 +175,33 @@ def _check_all_rows(wl, logits, b, wt, ids, label):
     assert rep.near_tie <= max(2, rep.rows // 1000), rep.summary()
 
 
-@pytest.mark.parametrize("M,splits", [(4096, 4), (8192, 2)])
+@pytest.mark.parametrize("M,splits", [(4096, 4), (6144, 2), (7001, 4), (8192, 4)])
 def test_fused_router_split_path_full_width(h7168, M, splits):
-    """64-row tiles of the 7168-wide router, every row against the oracle: 4
-    splits of 28 steps at 4096 tokens, 2 of 56 at 8192 (the full workload,
-    the library's default launch for it)."""
+    """The 7168-wide router on the split path, every row against the oracle:
+    64-row tiles at 4096 tokens (4 splits of 28 steps) and 6144 (2 of 56);
+    128-row tiles at 7001 tokens (4 splits, a ragged last tile) and 8192 (4
+    splits of 28 steps: the full workload, the library's default launch for
+    it)."""
     wl, hidden, w, b, logits = h7168
     assert mr.route_fused_router_workspace_size(M, wl.hidden_dim, wl.E) == \
         4 * 256 * M * splits
     log(f"[gpu] route_fused_router split path M={M} H={wl.hidden_dim} ({splits} splits)")
     wt, ids = _run(hidden[:M], w, b, wl.K, wl.G, wl.TG, wl.renormalize, "sigmoid", "top2sum")
     _check_all_rows(wl, logits[:M], b, wt, ids, f"{wl.name} M={M} split path ({splits} splits)")
+
+
+@pytest.mark.parametrize("M,H,G,TG,K,scoring,rule,bias", [
+    (6500, 512, 8, 4, 8, "sigmoid", "top2sum", True),   # 51 tiles of 128 rows, 4 splits
+    (6145, 256, 1, 1, 6, "softmax", "max", False),      # 49 tiles, 4 one-step splits
+])
+def test_fused_router_128_row_tiles(M, H, G, TG, K, scoring, rule, bias):
+    """The partial kernel's 128-row tiles (above 6144 tokens), every row
+    against the oracle, ragged last tile included."""
+    rng = np.random.default_rng(M + H)
+    hidden, w, b = _inputs(rng, M, H, bias=bias)
+    log(f"[gpu] route_fused_router 128-row tiles M={M} H={H} G={G} TG={TG} K={K} {scoring}")
+    wt, ids = _run(hidden, w, b, K, G, TG, True, scoring, rule)
+    _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, True, scoring, rule)
 
 
 # every epilogue instantiation (scoring, bias, group rule) on every path:
