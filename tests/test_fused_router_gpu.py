@@ -204,6 +204,27 @@ def test_fused_router_128_row_tiles(M, H, G, TG, K, scoring, rule, bias):
     _check(hidden, w, b, wt, ids, np.arange(M), K, G, TG, True, scoring, rule)
 
 
+def test_fused_router_128_row_tiles_workspace_contents():
+    """128-row tiles in 4 splits: a workspace full of arbitrary bytes, and
+    one reused across calls of other sizes, give the results of a fresh one,
+    every row against the oracle."""
+    rng = np.random.default_rng(29)
+    M, H = 7001, 512
+    hidden, w, b = _inputs(rng, M, H)
+    need = mr.route_fused_router_workspace_size(M, H, 256)
+    assert need == 4 * 256 * M * 4  # 55 tiles of 128 rows, 4 splits of 2 steps
+    ws = torch.from_numpy(rng.integers(0, 256, need, dtype=np.uint8)).to("cuda")
+    log(f"[gpu] route_fused_router 128-row tiles M={M} H={H}: arbitrary workspace bytes, reuse")
+    first = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    _check(hidden, w, b, first[0], first[1], np.arange(M), 8, 8, 4, True, "sigmoid", "top2sum")
+    smaller = _run(hidden[:6500], w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    again = _run(hidden, w, b, 8, 8, 4, True, "sigmoid", "top2sum", workspace=ws)
+    fresh = _run(hidden[:6500], w, b, 8, 8, 4, True, "sigmoid", "top2sum")
+    assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+    assert np.array_equal(smaller[0], fresh[0]) and np.array_equal(smaller[1], fresh[1])
+    assert np.array_equal(smaller[1], first[1][:6500])
+
+
 # every epilogue instantiation (scoring, bias, group rule) on every path:
 # the single kernel, the split path reduced a block per row (8 splits) and
 # a wave per 8 rows (4 splits)
