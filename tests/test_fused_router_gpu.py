@@ -82,6 +82,8 @@ def test_fused_router_biased_k_below_eight(K, G, TG, path):
     (200, 256, 1, 1, 2, "softmax", "max", False, False, 30.0),   # top-2 softmax, cap 30
     (77, 512, 1, 1, 1, "softmax", "max", False, False, 5.0),     # top-1 softmax
     (96, 128, 8, 4, 8, "sigmoid", "top2sum", True, True, 2.0),   # a cap that saturates
+    (3000, 256, 1, 1, 4, "softmax", "max", False, False, 5.0),   # 64-row tiles, 4 splits
+    (6200, 256, 8, 4, 8, "sigmoid", "top2sum", True, True, 30.0),  # 128-row tiles, 4 splits
 ])
 def test_fused_router_softcap(M, H, G, TG, K, scoring, rule, bias, renorm, cap):
     """Soft-capped logits: the oracle caps its exact logits in double."""
