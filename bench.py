@@ -246,6 +246,8 @@ def measure_all(out_path=None):
     routing_case("grouped_softmax_e160")
     for M in BIASED_GROUPED_M_SWEEP:
         routing_case("biased_grouped_e256", M)
+    results.append(steady_state_case(stream))
+    eprint(json.dumps(results[-1]))
 
     wl = WORKLOADS["fused_router_h7168"]
     hidden, w = make_router_inputs(wl)
@@ -447,6 +449,60 @@ def measure_all(out_path=None):
     return results
 
 
+STEADY_REPEAT = 32  # 32 x 65536 tokens in one launch
+
+
+def steady_inputs():
+    """The 65536-token headline logits repeated 32 times on the device (1 GiB
+    of bf16, more than the last-level cache), the bias and output buffers."""
+    import numpy as np
+    import torch
+
+    from workloads import WORKLOADS, make_bias, make_logits
+    wl = WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda", 0)
+    x = torch.from_numpy(make_logits(wl).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = x.repeat(STEADY_REPEAT, 1)
+    b = torch.from_numpy(make_bias(wl)).to(dev)
+    M = x.shape[0]
+    w = torch.empty(M, wl.K, device=dev)
+    ids = torch.empty(M, wl.K, dtype=torch.int32, device=dev)
+    return wl, x, b, w, ids
+
+
+def steady_state_case(stream):
+    """The headline kernel on 32x the headline tokens in one launch: the
+    per-65536-token cost once the launch's start-up and tail are spread
+    over many tiles."""
+    import moe_expert_routing_amd as mr
+    wl, x, b, w, ids = steady_inputs()
+    M = x.shape[0]
+
+    def launch(i):
+        mr.route_biased_grouped_topk(x, b, wl.K, wl.G, wl.TG, wl.renormalize, w, ids,
+                                     stream=stream)
+    per_call, kern = time_calls(launch, 1, stream, steps=40, warmup=4)
+    nbytes = algorithmic_bytes(M, wl.E, wl.K, 2)
+    return {"workload": wl.name, "case": "steady state: one launch of 32 x 65536 tokens",
+            "M": M, "us_per_call": per_call, "kernel_us": kern,
+            "us_per_65536_tokens": kern * 65536 / M, "tokens_per_s": M / (kern * 1e-6),
+            "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
+            "frac_hbm_kernel": nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
+def steady_run(calls=3):
+    """A few launches of the headline kernel on 32x its tokens: the program
+    profiled for the steady-state clock and VALU counters."""
+    import torch
+
+    import moe_expert_routing_amd as mr
+    wl, x, b, w, ids = steady_inputs()
+    for _ in range(calls):
+        mr.route_biased_grouped_topk(x, b, wl.K, wl.G, wl.TG, wl.renormalize, w, ids)
+    torch.cuda.synchronize()
+    print(json.dumps({"steady_run": "done", "calls": calls, "tokens": x.shape[0]}), flush=True)
+
+
 def profile_run(calls=5):
     """A few calls of every workload's kernels, each on its own input set
     where it reads enough to leave the last-level cache, with no timing
@@ -532,6 +588,8 @@ def main():
                     help="only run a 1 GiB device copy (for HBM byte counter scaling)")
     ap.add_argument("--profile-run", action="store_true",
                     help="only run a few calls of every workload (for rocprofv3 passes)")
+    ap.add_argument("--steady-run", action="store_true",
+                    help="only run a few headline launches of 32x its tokens (for rocprofv3)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -543,6 +601,9 @@ def main():
         return
     if args.profile_run:
         profile_run()
+        return
+    if args.steady_run:
+        steady_run()
         return
 
     import numpy as np
