@@ -32,7 +32,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
                 f"failures={len(rep.failures)} strict={'ok' if rep.strict_ok else 'NO'}")
         lines.append(line)
         tr.write_line(line)
-    out = os.path.join(ROOT, "gpurun_out")
-    if os.path.isdir(out):
-        with open(os.path.join(out, "parity_by_workload.txt"), "w") as f:
+    out = os.environ.get("MOE_ROUTE_PARITY_OUT")  # optional copy of these lines
+    if out:
+        with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
