@@ -89,7 +89,7 @@ def cpu_model():
 
 
 def host_cores():
-    """Cores this process may run on, at most 16 (a one-GPU machine's share)."""
+    """Cores this process may run on, at most 16 (the host share of one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

@@ -1,4 +1,4 @@
-"""The parity checker itself: it accepts the oracle's own answer, accepts a
+"""The parity comparison itself: it accepts the oracle's own answer, accepts a
 near-tie resolved the other way, and rejects real mistakes."""
 import numpy as np
 
