@@ -64,6 +64,7 @@ template <int ROWS> struct ARing {
     static constexpr int kAhead = kStages - 1;
     static constexpr int kCopies = kBytes / 1024;        // 4, 8 or 16 wave loads per step
     static_assert(kAhead >= kFrWAhead, "hidden states run at least as far ahead as W");
+    static_assert(kCopies * (kAhead - 1) <= 63, "a wait counts at most 63 loads");
     static_assert(kStages * kBytes + kFrWStages * kFrWBytes + (ROWS == 32 ? kFrE * 4 : 0) <=
                       160 * 1024,
                   "LDS of one workgroup");
