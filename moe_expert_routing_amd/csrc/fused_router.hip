@@ -33,6 +33,7 @@
 
 #include "route_common.hpp"
 #include "route_internal.h"
+#include "lds_copy.hpp"
 #include "route_tile.hpp"
 
 namespace moe_route {
@@ -75,41 +76,8 @@ static_assert(ARing<kFrRows>::kStages == kFrAStages && ARing<kFrRows>::kBytes ==
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-// Direct-to-LDS copies (global_load_lds_dwordx4): lane l copies 16 bytes from
-// its global address to LDS byte lds + 16 l (lds goes in M0).  They are inline asm
-// so that the compiler neither waits for them on its own (its conservative
-// waits drain the whole ring) nor counts them; the ring below waits for them
-// explicitly, and the loop holds no other vector-memory loads.  The
-// instruction writes no register, so nothing of the wave is overwritten
-// while a copy is in flight.
-__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds)
-                 : "memory");
-}
-__device__ __forceinline__ void lds_copy16(const void* base, uint32_t offset, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(offset), "s"(base),
-                 "{m0}"(lds) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)p));
-}
-
-// Workgroup barrier without a memory fence.  A fence here would make every
-// wave wait for all of its copies still in flight (they write LDS); the ring
-// instead waits explicitly for exactly the copies a step consumes.
-__device__ __forceinline__ void barrier_no_fence() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // Swizzles of the 16-byte chunk index inside an LDS row.
 // A rows (8 chunks): chunk c of row m lives at c ^ ((m >> 1) & 7).

@@ -5,14 +5,17 @@
 // (each logit a product summed along the hidden dimension) followed by
 // optional soft-capping and a softmax top-1/top-2, and sends small batches
 // and routers with at most 8 experts to it.  Here two kernels serve these
-// expert counts at every batch size; both read the hidden states once, which
+// expert counts at every batch size; all read the hidden states once, which
 // bounds them (2H bytes per token against 2EH multiply-adds):
 //
-//  - an MFMA kernel (hidden_dim <= 8192): 16-token tiles on
-//    v_mfma_f32_16x16x32_bf16, W held in registers (described below);
+//  - MFMA kernels (hidden_dim <= 8192): 16-token tiles on
+//    v_mfma_f32_16x16x32_bf16, W held in registers (described below).  With
+//    hidden_dim a multiple of 1024 the hidden states come through a ring of
+//    LDS stages in whole 1 KiB row runs; otherwise each lane loads its MFMA
+//    operand straight from global memory;
 //  - a vector-ALU kernel: bf16 pairs on v_dot2_f32_bf16, used for more than
-//    8192 hidden units, and for 8 experts below 4096 tokens, where its
-//    8-token blocks spread over more compute units than 16-token tiles do.
+//    8192 hidden units, and for 8 experts with few tokens, where its 8-token
+//    blocks spread over more compute units than 16-token tiles do.
 //
 // Vector-ALU layout.  A block of 4 waves routes groups of T = 8 tokens
 // (persistent blocks stride over the groups); the waves take turns over
@@ -32,6 +35,7 @@
 #include <algorithm>
 
 #include "route_common.hpp"
+#include "lds_copy.hpp"
 #include "route_internal.h"
 
 namespace moe_route {
@@ -262,10 +266,9 @@ route_status_t launch_sr(const FusedProblem& f) {
 // K rounds of a butterfly argmax by (c desc, index asc), weights s of the
 // picks added in pick order; the pick of rank k is stored by its lane.
 template <int E, bool SOFTMAX, bool BIAS>
-__device__ __forceinline__ void route_lanes16(float x, int j, bool store,
-                                              BiasRef bias, int K, int renorm,
-                                              float* __restrict__ w_row,
-                                              int32_t* __restrict__ id_row) {
+__device__ __forceinline__ void route_lanes16_b(float x, int j, bool store, float bj, int K,
+                                                int renorm, float* __restrict__ w_row,
+                                                int32_t* __restrict__ id_row) {
     const bool live = j < E;
     float s;
     if constexpr (SOFTMAX) {
@@ -280,7 +283,7 @@ __device__ __forceinline__ void route_lanes16(float x, int j, bool store,
     } else {
         s = sigmoid_f32(x);
     }
-    const float c = BIAS && live ? s + bias_at(bias, j) : s;
+    const float c = BIAS && live ? s + bj : s;
     bool open = live;  // not picked yet
     int rank = -1;
     float tot = 0.f;
@@ -300,6 +303,15 @@ __device__ __forceinline__ void route_lanes16(float x, int j, bool store,
         w_row[rank] = renorm ? s / tot : s;
         id_row[rank] = j;
     }
+}
+// The same with the bias entry of lane j read here.
+template <int E, bool SOFTMAX, bool BIAS>
+__device__ __forceinline__ void route_lanes16(float x, int j, bool store,
+                                              BiasRef bias, int K, int renorm,
+                                              float* __restrict__ w_row,
+                                              int32_t* __restrict__ id_row) {
+    const float bj = BIAS && j < E ? bias_at(bias, j) : 0.0f;
+    route_lanes16_b<E, SOFTMAX, BIAS>(x, j, store, bj, K, renorm, w_row, id_row);
 }
 
 // ---- MFMA variant (hidden_dim <= 8192)
@@ -474,6 +486,198 @@ route_status_t launch_sm_nb(const FusedProblem& f) {
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 
+// ---- MFMA variant with a hidden-state ring in LDS (hidden_dim a multiple of
+// 1024, at most 8192)
+//
+// The kernel above loads its A operands straight from global memory in the
+// MFMA layout: a (token, quarter) lane per 16 bytes, so every wave load
+// touches 16 rows, 64 bytes of each.  Here the hidden states of a 16-token
+// tile come through LDS, 1024 hidden units (a chunk) at a time: every wave
+// copy (global_load_lds_dwordx4) is 1 KiB of one row, and the fragments are
+// read from LDS in the MFMA layout.  A ring of 4 chunk stages keeps 3 chunks
+// in flight ahead of the MFMAs, running on across the block's tiles.  Inside
+// a copy, lane l fetches 16-byte piece l ^ (row mod 16) of the copy's run, so
+// that the 16 rows of a fragment read land in different LDS banks.  W sits in
+// registers as in the kernel above (fragment f of H with wave f mod 8); the
+// 8 waves' partial tiles are added in LDS in wave order and routed by 16
+// lanes per token.
+constexpr int kRgChunk = 1024;                                       // hidden units
+constexpr int kRgStages = 4;
+constexpr int kRgAhead = kRgStages - 1;                              // chunks in flight
+constexpr int kRgStageBytes = kSmTile * kRgChunk * 2;                // 32 KiB
+constexpr int kRgCopies = kRgStageBytes / 1024 / kSmWaves;           // 4 a wave a chunk
+constexpr int kRgFrags = kRgChunk / 32 / kSmWaves;                   // 4 a wave a chunk
+static_assert(kRgCopies == 4 && kSmTile == 2 * kSmWaves, "wave w copies rows 2w, 2w + 1");
+static_assert(kRgCopies * (kRgAhead - 1) <= 63, "a wait counts at most 63 loads");
+static_assert(kSmWaves * kSmBatch * 1024 <= kRgStageBytes, "the W images fit one stage");
+
+// LDS barrier that leaves the copies in flight alone (waits for this wave's
+// LDS accesses only).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int E, int NCH, bool SOFTMAX, bool BIAS>
+__global__ __launch_bounds__(kSmThreads) void small_router_ring_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w,
+    BiasRef bias, int64_t M, int K, int renorm, float cap,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out) {
+    constexpr int H = NCH * kRgChunk;
+    constexpr int FM = NCH * kRgFrags;  // fragments of W per wave
+    __shared__ __align__(1024) unsigned char ring[kRgStages][kRgStageBytes];
+    __shared__ float part[kSmWaves][kSmTile * 16];
+
+    const int t = threadIdx.x, lane = t % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int i16 = lane % 16, q = lane / 16;
+    const int64_t tiles = (M + kSmTile - 1) / kSmTile;
+    const int64_t steps = ((tiles - 1 - blockIdx.x) / gridDim.x + 1) * NCH;  // blockIdx.x < tiles
+
+    // The copies of step s (chunk s mod NCH of the block's tile s / NCH):
+    // copy u is half u % 2 of row 2 wv + u / 2's run (rows past M read row
+    // M-1, never stored).
+    auto issue = [&](int64_t s, int stage) {
+        const int64_t g = blockIdx.x + (s / NCH) * gridDim.x;
+        const int c = (int)(s % NCH);
+#pragma unroll
+        for (int u = 0; u < kRgCopies; ++u) {
+            const int r = 2 * wv + u / 2, j = u % 2;
+            const int64_t row = min(g * kSmTile + r, M - 1);
+            const int piece = 64 * j + (lane ^ (r & 15));
+            lds_copy16(hidden + row * H + c * kRgChunk + 8 * piece,
+                       lds_addr(ring[stage] + r * (2 * kRgChunk) + 1024 * j));
+        }
+    };
+    // The bias entry of expert i16 (the lanes that route take expert t % 16),
+    // loaded first: the waits of the W loads below then cover it, and no
+    // wait for it is left inside the loop (one there would drain the ring).
+    const float bj = BIAS && i16 < E ? bias_at(bias, i16) : 0.0f;
+    issue(0, 0);
+
+    // W into registers: wf[i] holds fragment wv + 8 i (units 32 (wv + 8 i)
+    // ..), built through a per-wave LDS image of 32 rows x 16 experts in the
+    // last ring stage, which the first copies do not use.
+    bf16x8 wf[FM];
+    {
+        unsigned char* img = ring[kRgAhead] + wv * (kSmBatch * 1024);
+        const int row = lane / 2, half = lane % 2;
+        // with 8 experts the second 16 bytes of an image row are zeros (both
+        // halves load the row's 16 bytes; the second is masked)
+        const uint32_t keep = E == 16 || half == 0 ? ~0u : 0u;
+        uint4 raw[2][kSmBatch];  // round rr + 1 loads while round rr is turned
+        auto wload = [&](int rr, uint4 (&dst)[kSmBatch]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i) {
+                const int k = 32 * (wv + kSmWaves * (kSmBatch * rr + i)) + row;
+                dst[i] = *reinterpret_cast<const uint4*>(w + (int64_t)k * E + (E == 16 ? 8 * half : 0));
+            }
+        };
+        wload(0, raw[0]);
+#pragma unroll
+        for (int rr = 0; rr < FM / kSmBatch; ++rr) {
+            if (rr + 1 < FM / kSmBatch) wload(rr + 1, raw[(rr + 1) % 2]);
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i) {
+                const uint4 v = raw[rr % 2][i];
+                *reinterpret_cast<uint4*>(img + 1024 * i + 16 * lane) =
+                    make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < kSmBatch; ++i) {
+                i16x4 h2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int off = 1024 * i + 32 * (8 * q + 4 * h + i16 / 4) + 8 * (i16 % 4);
+                    h2[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(img + off));
+                }
+                wf[kSmBatch * rr + i] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            wave_lds_sync();
+        }
+    }
+    for (int s = 1; s < kRgAhead; ++s) issue(min<int64_t>(s, steps - 1), s);
+
+    // Step s: wait for this wave's copies of step s (those of the next
+    // kRgAhead - 1 steps may stay in flight), then a barrier makes every
+    // wave's copies visible and frees the stage of step s - 1 for step
+    // s + kRgAhead.  Copies past the last step repeat it into a stage that
+    // is never read again.
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    int stage = 0;
+    for (int64_t tt = 0; tt * NCH < steps; ++tt) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {  // unrolled: wf is indexed with constants
+            const int64_t s = tt * NCH + c;
+            wait_vmcnt<kRgCopies * (kRgAhead - 1)>();
+            barrier_no_fence();
+            issue(min(s + kRgAhead, steps - 1), (stage + kRgAhead) % kRgStages);
+            const unsigned char* st = ring[stage];
+#pragma unroll
+            for (int i = 0; i < kRgFrags; ++i) {
+                const int gc = 4 * (wv + kSmWaves * i) + q;  // 16-byte piece of the row's run
+                const int off = i16 * (2 * kRgChunk) + 1024 * (gc >> 6) + 16 * ((gc & 63) ^ i16);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + off);
+                if (i % 2 == 0)
+                    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[kRgFrags * c + i], c0, 0, 0, 0);
+                else
+                    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wf[kRgFrags * c + i], c1, 0, 0, 0);
+            }
+            stage = stage + 1 == kRgStages ? 0 : stage + 1;
+        }
+        // D layout: lane (expert i16, quarter q) holds tokens 4q .. 4q+3
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wv][(4 * q + r) * 16 + i16] = c0[r] + c1[r];
+        lds_barrier();
+        // thread t < 256: token t / 16, expert t % 16; waves added in order
+        float v = 0.f;
+        if (t < kSmTile * 16) {
+#pragma unroll
+            for (int x = 0; x < kSmWaves; ++x) v += part[x][t];
+            if (cap != 0.0f) v = cap * tanh_f32(v / cap);
+        }
+        lds_barrier();  // part is free for the next tile
+        const int64_t row = (blockIdx.x + tt * gridDim.x) * kSmTile + t / 16;
+        if (t < kSmTile * 16)
+            route_lanes16_b<E, SOFTMAX, BIAS>(v, t % 16, row < M, bj, K, renorm,
+                                              w_out + row * K, id_out + row * K);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { c0[r] = 0.f; c1[r] = 0.f; }
+    }
+    wait_vmcnt<0>();  // no copy is left in flight when the workgroup ends
+}
+
+template <int E, int NCH, bool SOFTMAX, bool BIAS>
+route_status_t launch_rg_nch(const FusedProblem& f) {
+    const RouteProblem& p = f.route;
+    const int64_t tiles = (f.M + kSmTile - 1) / kSmTile;
+    const int64_t blocks = std::min<int64_t>(tiles, (int64_t)device_cu_count());
+    hipLaunchKernelGGL((small_router_ring_kernel<E, NCH, SOFTMAX, BIAS>), dim3((unsigned)blocks),
+                       dim3(kSmThreads), 0, p.stream, static_cast<const uint16_t*>(f.hidden),
+                       static_cast<const uint16_t*>(f.w), p.bias, f.M, p.K, p.renorm ? 1 : 0,
+                       f.softcap, p.weights, p.ids);
+    return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
+}
+
+bool ring_shape(const FusedProblem& f) {
+    return f.H % kRgChunk == 0 && f.H <= kSmHMax;
+}
+
+template <int E, bool SOFTMAX, bool BIAS>
+route_status_t launch_rg(const FusedProblem& f) {
+    switch (f.H / kRgChunk) {
+        case 1: return launch_rg_nch<E, 1, SOFTMAX, BIAS>(f);
+        case 2: return launch_rg_nch<E, 2, SOFTMAX, BIAS>(f);
+        case 3: return launch_rg_nch<E, 3, SOFTMAX, BIAS>(f);
+        case 4: return launch_rg_nch<E, 4, SOFTMAX, BIAS>(f);
+        case 5: return launch_rg_nch<E, 5, SOFTMAX, BIAS>(f);
+        case 6: return launch_rg_nch<E, 6, SOFTMAX, BIAS>(f);
+        case 7: return launch_rg_nch<E, 7, SOFTMAX, BIAS>(f);
+        default: return launch_rg_nch<E, 8, SOFTMAX, BIAS>(f);
+    }
+}
+
 template <int E, bool SOFTMAX, bool BIAS>
 route_status_t launch_sm(const FusedProblem& f) {
     const int nf = (f.H + 31) / 32;
@@ -493,9 +697,15 @@ route_status_t launch_sm(const FusedProblem& f) {
 template <int E>
 route_status_t launch_sr_e(const FusedProblem& f) {
     const RouteProblem& p = f.route;
-    // One MFMA block per 16-token tile leaves compute units idle below 256
+    // One MFMA block per 16-token tile leaves compute units idle with few
     // tiles; with 8 experts the vector-ALU kernel (8 tokens per block, half
-    // the work per token of 16 experts) measured faster there.
+    // the work per token of 16 experts) measured faster below 64 tiles with
+    // the LDS ring (at 1024 tokens 6.6 against 7.8 us, at 512 even) and below
+    // 256 tiles with the direct loads.
+    if (ring_shape(f) && (E == 16 || f.M >= 64 * kSmTile)) {
+        if (p.scoring == ROUTE_SOFTMAX) return launch_rg<E, true, false>(f);
+        return p.bias.p ? launch_rg<E, false, true>(f) : launch_rg<E, false, false>(f);
+    }
     const bool mfma = f.H <= kSmHMax && (E == 16 || f.M >= 256 * kSmTile);
     if (mfma) {
         if (p.scoring == ROUTE_SOFTMAX) return launch_sm<E, true, false>(f);

@@ -49,13 +49,18 @@ def _run_check(hidden, w, b, E, K, scoring, renorm, cap, label=None, workspace=N
     (50, 6144, 16, 4, "softmax", False, True, 0.0, 1.0),    # 16 experts
     (19, 1000, 16, 2, "sigmoid", False, False, 2.0, 3.0),   # 16 experts, saturating cap
     (256, 512, 16, 16, "softmax", False, False, 0.0, 1.0),  # K = E = 16
-    (4000, 7168, 16, 2, "softmax", False, True, 0.0, 1.0),  # 250 tiles, 28 fragments a wave
+    (4000, 7168, 16, 2, "softmax", False, True, 0.0, 1.0),  # LDS ring: 250 tiles, 7 chunks
     (4100, 1000, 8, 2, "softmax", False, False, 5.0, 3.0),  # 8 experts on MFMA, ragged H
     # MFMA kernel, every batch count (4 fragments of 32 units a batch, 8 waves)
-    (70, 2048, 16, 2, "softmax", False, True, 0.0, 1.0),    # 2 batches
-    (70, 3072, 16, 4, "sigmoid", True, True, 0.0, 1.0),     # 3 batches
-    (70, 5120, 16, 2, "softmax", False, False, 30.0, 1.0),  # 5 batches
-    (70, 8192, 16, 4, "softmax", False, True, 0.0, 1.0),    # 8 batches (reloads from scratch)
+    (70, 1056, 16, 2, "softmax", False, True, 0.0, 1.0),    # 2 batches
+    (70, 2080, 16, 4, "sigmoid", True, True, 0.0, 1.0),     # 3 batches
+    (70, 4128, 16, 2, "softmax", False, False, 30.0, 1.0),  # 5 batches
+    (70, 8192, 16, 4, "softmax", False, True, 0.0, 1.0),    # LDS ring: 8 chunks
+    (70, 3072, 16, 4, "sigmoid", True, True, 0.0, 1.0),     # LDS ring: 3 chunks, bias
+    (4100, 2048, 8, 2, "sigmoid", True, True, 0.0, 1.0),    # LDS ring, 8 experts, ragged tile
+    (4096, 1024, 8, 1, "softmax", False, False, 30.0, 1.0), # LDS ring, one chunk, cap
+    (1500, 3072, 8, 2, "softmax", False, True, 5.0, 1.0),   # LDS ring, 8 experts from 1024 tokens
+    (1000, 4096, 16, 4, "sigmoid", True, False, 0.0, 3.0),  # LDS ring, 4 chunks, wide logits
     (70, 8000, 16, 2, "sigmoid", False, True, 0.0, 1.0),    # 8 batches, ragged H
     (33, 9000, 8, 2, "softmax", False, False, 30.0, 1.0),   # H > 8192: vector-ALU kernel
     (20, 8704, 16, 3, "sigmoid", True, True, 0.0, 1.0),     # H > 8192, 16 experts
