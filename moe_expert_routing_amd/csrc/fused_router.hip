@@ -291,8 +291,8 @@ __global__ __launch_bounds__(kFrThreads) void fused_router_kernel(
     const int64_t row = m0 + r;
     const float* lrow = L + r * kFrE;
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
-        x, sub, rw_in_wave, row < M, row, S + r * kFrE, s_bias, kp, TG, K, renorm, w_out,
-        id_out, [&](int e) { return lrow[e]; },
+        x, sub, rw_in_wave, row < M, S + r * kFrE, s_bias, kp, TG, K, renorm,
+        w_out + min(row, M - 1) * K, id_out + min(row, M - 1) * K, [&](int e) { return lrow[e]; },
         [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
 }
 
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
         x[4 * v] = d.x; x[4 * v + 1] = d.y; x[4 * v + 2] = d.z; x[4 * v + 3] = d.w;
     }
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
-        x, sub, rw, rw == 0, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
+        x, sub, rw, rw == 0, S[rw], s_bias, kp, TG, K, renorm, w_out + row * K, id_out + row * K,
         [&](int e) { return L[e]; },
         [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
 }
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kWave) void fr_reduce_route_rows_kernel(
     // with one lane per row, so not here; it stays exact for any later use)
     const float* rsrc = part + rrow * kFrE;
     route_rows<8, 32, SOFTMAX, BIAS, GRP, (GRP ? 2 : 1), (GRP ? 4 : 5), 8>(
-        x, sub, rw, row < M, row, S[rw], s_bias, kp, TG, K, renorm, w_out, id_out,
+        x, sub, rw, row < M, S[rw], s_bias, kp, TG, K, renorm, w_out + rrow * K, id_out + rrow * K,
         [&](int e) {
             float v = rsrc[e];
             for (int sp = 1; sp < nsplit; ++sp) v += rsrc[sp * split_stride + e];

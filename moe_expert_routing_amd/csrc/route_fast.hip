@@ -150,6 +150,10 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave, 3) void route_fast_kernel(
         kp = key_params(0.0f, 1.0f);
     }
 
+    // The row's outputs move by a fixed stride from one tile of the wave to
+    // the next (no multiply by the runtime K in the loop).
+    const int64_t out_step = tstride * RPW * K;
+    int64_t out_off = (tile * RPW + rw) * K;
     auto route_tile = [&](const RawLane<T, VPL>& r, int64_t t) {
         const int64_t row = t * RPW + rw;
         const bool valid = row < M;
@@ -157,9 +161,10 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave, 3) void route_fast_kernel(
         r.unpack(x);
         const T* xr = logits + (valid ? row : 0) * E;
         route_rows<LPR, VPL, SOFTMAX, BIAS, GRP, SPLIT, TL, KMAX>(
-            x, sub, rw, valid, row, my_row, s_bias, kp, TG, K, renorm, w_out, id_out,
-            [&](int e) { return load_one<T>(xr, e); },
+            x, sub, rw, valid, my_row, s_bias, kp, TG, K, renorm, w_out + out_off,
+            id_out + out_off, [&](int e) { return load_one<T>(xr, e); },
             [&](int e) { return BIAS ? bias_at(bias, e) : 0.0f; });
+        out_off += out_step;
     };
     // The second tile is requested only once the first has arrived: at the
     // start every wave of the grid requests at once, and second tiles

@@ -251,8 +251,9 @@ __device__ __forceinline__ float lane_score(float x, float mx) {
 }
 
 // Route the rows of one wave tile.  Lane `sub` of row-in-wave `rw` brings the
-// fp32 logits x[0..VPL) of experts [sub*VPL, sub*VPL + VPL) of token `row`
-// (valid == false past the last token: computed, never stored).  my_row is
+// fp32 logits x[0..VPL) of experts [sub*VPL, sub*VPL + VPL) of its token,
+// whose K weights and ids go to w_row[0..K) and id_row[0..K) (valid ==
+// false past the last token: computed, never stored).  my_row is
 // this row's E-float LDS scratch (LPR > 1); s_bias the staged bias offsets
 // (sel_offset of each expert's bias) in LDS, in the bias_elem layout (BIAS);
 // logit_of(e) returns the fp32 logit of expert e of this row and bias_of(e)
@@ -262,10 +263,10 @@ __device__ __forceinline__ float lane_score(float x, float mx) {
 template <int LPR, int VPL, bool SOFTMAX, bool BIAS, int GRP /*0 none, 1 max, 2 top2*/, int SPLIT,
           int TL, int KMAX, typename LogitFn, typename BiasFn>
 __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const int rw,
-                                           const bool valid, const int64_t row, float* my_row,
+                                           const bool valid, float* my_row,
                                            const float* s_bias, const KeyParams& kp, const int TG,
-                                           const int K, const int renorm, float* __restrict__ w_out,
-                                           int32_t* __restrict__ id_out, LogitFn logit_of,
+                                           const int K, const int renorm, float* __restrict__ w_row,
+                                           int32_t* __restrict__ id_row, LogitFn logit_of,
                                            BiasFn bias_of) {
     constexpr int E = LPR * VPL;
     constexpr int NC = GRP ? VPL / SPLIT : VPL;    // candidates per lane in the list step
@@ -617,8 +618,8 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
             const int r = s * LPR + sub;
             const int o = s == 0 ? slot0 : r;
             if (r < K) {
-                w_out[row * K + o] = renorm ? wsl[s] * inv_tot : wsl[s];
-                id_out[row * K + o] = pick[s];
+                w_row[o] = renorm ? wsl[s] * inv_tot : wsl[s];
+                id_row[o] = pick[s];
             }
         }
     }
