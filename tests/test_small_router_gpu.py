@@ -62,6 +62,7 @@ def _run_check(hidden, w, b, E, K, scoring, renorm, cap, label=None, workspace=N
     (1500, 3072, 8, 2, "softmax", False, True, 5.0, 1.0),   # LDS ring, 8 experts from 1024 tokens
     (20000, 2048, 8, 2, "softmax", False, True, 0.0, 1.0),  # LDS ring, ~5 tiles a block
     (9001, 1024, 16, 4, "sigmoid", True, True, 0.0, 1.0),   # LDS ring, 3 tiles a block, ragged
+    (1, 2048, 16, 4, "sigmoid", True, True, 0.0, 1.0),      # LDS ring, a single token
     (1000, 4096, 16, 4, "sigmoid", True, False, 0.0, 3.0),  # LDS ring, 4 chunks, wide logits
     (70, 8000, 16, 2, "sigmoid", False, True, 0.0, 1.0),    # 8 batches, ragged H
     (33, 9000, 8, 2, "softmax", False, False, 30.0, 1.0),   # H > 8192: vector-ALU kernel
