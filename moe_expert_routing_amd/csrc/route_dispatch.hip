@@ -25,14 +25,17 @@
 //             each column into exclusive offsets across blocks and writes
 //             the expert's total;
 //   3. place: each block scans the totals into expert offsets (block 0 also
-//             writes counts and offsets), recounts its chunk per wave, so that every wave
-//             starts from its own cursor per expert (the expert offset plus
-//             the counts of earlier blocks and earlier waves), then walks its
-//             part 64 assignments at a time.  Lanes with the same expert find
-//             each other with one ballot per bit of the expert id; a lane's
-//             rank among them (mbcnt) plus its wave's cursor is its sorted
-//             position, so equal ids keep their order without ordered
-//             atomics.
+//             writes counts and offsets) and its own per-expert counts into
+//             block slots (its assignments in expert order, each wave
+//             starting from its own cursor per expert), then walks its part
+//             64 assignments at a time.  Lanes with the same expert find each
+//             other with one ballot per bit of the expert id; a lane's rank
+//             among them (mbcnt) plus its wave's cursor is its block slot, so
+//             equal ids keep their order without ordered atomics.  The
+//             scatter index is stored at once; the slots go through LDS and
+//             are stored in slot order, so that each expert's run of the
+//             block lands in consecutive gather and weight entries instead of
+//             one scattered 4-byte store per assignment.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -159,10 +162,35 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     }
 }
 
-// LDS layout of the place kernel: offsets [E + 1], carries [kDispWaves], then
-// (16-byte aligned) the per-wave counts and cursors, or first the coarse
-// partials.
-__host__ __device__ constexpr int place_cur_offset(int E) { return (E + 1 + kDispWaves + 3) & ~3; }
+// LDS layout of the place kernel, in ints: expert offsets [E + 1], scan
+// carries [2 kDispWaves], per-expert global bases [E]; then, 16-byte
+// aligned, the per-wave counts and cursors [kDispWaves][E], and a region
+// that first holds the coarse partials [2 G][E] and the recount [E] (COARSE)
+// and afterwards the block's assignments in sorted order [kBlockChunk] and
+// their weights [kBlockChunk].  At most 60 KiB (E = 1024).
+struct PlaceLds {
+    int off, wsum, gb, cnt, slot, slot_w, pre, all, rc, ints;
+};
+__host__ __device__ constexpr PlaceLds place_lds(int E, int G) {
+    PlaceLds l{};
+    l.off = 0;
+    l.wsum = E + 1;
+    l.gb = l.wsum + 2 * kDispWaves;
+    l.cnt = (l.gb + E + 3) & ~3;
+    l.slot = l.cnt + kDispWaves * E;
+    l.slot_w = l.slot + kBlockChunk;
+    l.pre = l.slot;
+    l.all = l.pre + G * E;
+    l.rc = l.all + G * E;
+    const int tail = G > 0 ? 2 * G * E + E : 0;
+    l.ints = l.slot + (tail > 2 * kBlockChunk ? tail : 2 * kBlockChunk);
+    return l;
+}
+static_assert(place_lds(kMaxExperts, kDispThreads / (kMaxExperts / 4)).ints * 4 <= 64 * 1024,
+              "place kernel LDS within 64 KiB");
+constexpr int kLocalBits = 11;  // assignment index within a block
+static_assert(kBlockChunk == 1 << kLocalBits, "block-local index width");
+static_assert(kMaxExperts << kLocalBits <= 0x7fffffff, "expert and local index in one int");
 
 // COARSE: cnt is the coarse matrix [C][E] (E a multiple of 4, 16-byte
 // aligned rows, C * E <= kCoarseMaxInts) and totals is unused; otherwise cnt
@@ -174,9 +202,14 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ gather,
     int32_t* __restrict__ scatter, float* __restrict__ sorted_w) {
     extern __shared__ int32_t smem[];
-    int32_t* s_off = smem;                     // [E + 1] expert offsets
-    int32_t* s_wsum = s_off + E + 1;           // [kDispWaves] scan carries
-    int32_t* s_cur = smem + place_cur_offset(E);  // [kDispWaves][E] counts, then cursors
+    const int G = COARSE ? kDispThreads / (E / 4) : 0;
+    const PlaceLds L = place_lds(E, G);
+    int32_t* s_off = smem + L.off;    // [E + 1] expert offsets
+    int32_t* s_wsum = smem + L.wsum;  // [2][kDispWaves] scan carries
+    int32_t* s_gb = smem + L.gb;      // [E] sorted position = s_gb[e] + block slot
+    int32_t* s_cnt = smem + L.cnt;    // [kDispWaves][E] counts, then block-slot cursors
+    int32_t* s_slot = smem + L.slot;  // [kBlockChunk] expert << kLocalBits | local index
+    float* s_slot_w = reinterpret_cast<float*>(smem + L.slot_w);  // [kBlockChunk]
     constexpr int kEPT = kMaxExperts / kDispThreads;  // experts per thread (<= 4)
     const int t = threadIdx.x;
     const int lane = t % kWave;
@@ -185,23 +218,25 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
     // a0 + 64 j, the expert totals (experts kEPT t ..), the block's row of
     // offsets across blocks (COARSE: the coarse matrix and the assignments
     // to recount)
-    const int64_t a0 = (int64_t)blockIdx.x * kBlockChunk + (int64_t)wv * kWaveChunk + lane;
+    const int64_t blk0 = (int64_t)blockIdx.x * kBlockChunk;
+    const int l0 = wv * kWaveChunk + lane;  // block-local index of assignment j = 0
     int32_t idv[kPerLane];
     float wv8[kPerLane];
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-        const int64_t a = a0 + (int64_t)j * kWave;
+        const int64_t a = blk0 + l0 + j * kWave;
         idv[j] = a < n ? ids[a] : -1;
         wv8[j] = (sorted_w && a < n) ? wts[a] : 0.0f;
     }
     int tot[kEPT], rowv[kEPT];
+    for (int i = t; i < kDispWaves * E; i += kDispThreads) s_cnt[i] = 0;
     if constexpr (COARSE) {
         // Thread t < Q * G reduces 16-byte quad q = t % Q of rows
         // r = g, g + G, ... (g = t / Q) into a before-my-row and an all-rows
         // partial; the G partials of an expert are added in LDS.  The
         // assignments of the preceding chunks of this block's coarse row are
-        // recounted into s_cur row 0.
-        const int Q = E / 4, G = kDispThreads / Q;
+        // recounted into s_rc.
+        const int Q = E / 4;
         const int c = blockIdx.x / kSubPerRow;
         const int q = t % Q, g = t / Q;
         int4 m[kCoarseRowsPerLane];
@@ -222,9 +257,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
                 const int o = (u * kPerLane + j) * kDispThreads + t;
                 rid[u][j] = o < nrc ? ids[rc0 + o] : -1;  // rc0 + o < n: earlier chunks are full
             }
-        int32_t* s_pre = s_cur;                    // [G][E] partials (rows before c)
-        int32_t* s_all = s_cur + G * E;            // [G][E] partials (all rows)
-        int32_t* s_rc = s_all + G * E;             // [E] recount
+        int32_t* s_pre = smem + L.pre;  // [G][E] partials (rows before c)
+        int32_t* s_all = smem + L.all;  // [G][E] partials (all rows)
+        int32_t* s_rc = smem + L.rc;    // [E] recount
         for (int e = t; e < E; e += kDispThreads) s_rc[e] = 0;
         if (g < G) {
             int4 pre = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
@@ -242,6 +277,9 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
 #pragma unroll
             for (int j = 0; j < kPerLane; ++j)
                 if (valid_id(rid[u][j], E)) atomicAdd(&s_rc[rid[u][j]], 1);
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j)
+            if (valid_id(idv[j], E)) atomicAdd(&s_cnt[wv * E + idv[j]], 1);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kEPT; ++i) {
@@ -257,7 +295,6 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
             tot[i] = a;
             rowv[i] = p;
         }
-        __syncthreads();  // s_cur is reused below
     } else {
         const int32_t* row = cnt + (int64_t)blockIdx.x * E;
 #pragma unroll
@@ -266,45 +303,81 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
             tot[i] = e < E ? totals[e] : 0;
             rowv[i] = e < E ? row[e] : 0;
         }
-    }
-    // expert offsets: exclusive scan of the totals over the block
-    int sum = 0;
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kEPT; ++i) sum += tot[i];
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += v;
+        for (int j = 0; j < kPerLane; ++j)
+            if (valid_id(idv[j], E)) atomicAdd(&s_cnt[wv * E + idv[j]], 1);
+        __syncthreads();
     }
-    if (lane == kWave - 1) s_wsum[wv] = incl;
-    for (int i = t; i < kDispWaves * E; i += kDispThreads) s_cur[i] = 0;
-    __syncthreads();
-    int run = incl - sum;
-    for (int q = 0; q < wv; ++q) run += s_wsum[q];
+    // per expert: the block's count and each wave's exclusive prefix in it
+    int wpre[kEPT][kDispWaves], bc[kEPT];
 #pragma unroll
     for (int i = 0; i < kEPT; ++i) {
         const int e = kEPT * t + i;
-        if (e < E) s_off[e] = run;
-        run += tot[i];
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < kDispWaves; ++q) {
+            wpre[i][q] = c;
+            c += e < E ? s_cnt[q * E + e] : 0;
+        }
+        bc[i] = c;
     }
-    if (t == kDispThreads - 1) s_off[E] = run;
-    int32_t* cur = s_cur + wv * E;
+    // exclusive scans over the experts of the totals (expert offsets) and of
+    // the block's counts (the block's own slots, in expert order)
+    int sum_t = 0, sum_b = 0;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
-        if (valid_id(idv[j], E)) atomicAdd(&cur[idv[j]], 1);
+    for (int i = 0; i < kEPT; ++i) {
+        sum_t += tot[i];
+        sum_b += bc[i];
+    }
+    int inc_t = sum_t, inc_b = sum_b;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int vt = __shfl_up(inc_t, o, kWave);
+        const int vb = __shfl_up(inc_b, o, kWave);
+        if (lane >= o) {
+            inc_t += vt;
+            inc_b += vb;
+        }
+    }
+    if (lane == kWave - 1) {
+        s_wsum[wv] = inc_t;
+        s_wsum[kDispWaves + wv] = inc_b;
+    }
     __syncthreads();
-    if (blockIdx.x == 0) {
+    int run_t = inc_t - sum_t, run_b = inc_b - sum_b, nblk = 0;
 #pragma unroll
-        for (int i = 0; i < kEPT; ++i) {
-            const int e = kEPT * t + i;
-            if (e < E) {
+    for (int q = 0; q < kDispWaves; ++q) {
+        const int vb = s_wsum[kDispWaves + q];
+        if (q < wv) {
+            run_t += s_wsum[q];
+            run_b += vb;
+        }
+        nblk += vb;  // the block's valid assignments
+    }
+#pragma unroll
+    for (int i = 0; i < kEPT; ++i) {
+        const int e = kEPT * t + i;
+        if (e < E) {
+            s_off[e] = run_t;
+            // sorted position of block slot s (expert e) = expert offset +
+            // earlier blocks' count + (s - first slot of e in the block)
+            s_gb[e] = run_t + rowv[i] - run_b;
+#pragma unroll
+            for (int q = 0; q < kDispWaves; ++q) s_cnt[q * E + e] = run_b + wpre[i][q];
+            if (blockIdx.x == 0) {
                 counts[e] = tot[i];
-                offsets[e] = s_off[e];
+                offsets[e] = run_t;
             }
         }
-        if (t == 0) offsets[E] = s_off[E];
+        run_t += tot[i];
+        run_b += bc[i];
     }
+    if (t == kDispThreads - 1) {
+        s_off[E] = run_t;
+        if (blockIdx.x == 0) offsets[E] = run_t;
+    }
+    __syncthreads();
     const int64_t nvalid = s_off[E];
     // sorted positions past the valid assignments
     for (int64_t p = nvalid + (int64_t)blockIdx.x * kDispThreads + t; p < n;
@@ -312,28 +385,15 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         gather[p] = -1;
         if (sorted_w) sorted_w[p] = 0.0f;
     }
-    // cursor of wave q for expert e: expert offset + earlier blocks + earlier waves
-#pragma unroll
-    for (int i = 0; i < kEPT; ++i) {
-        const int e = kEPT * t + i;
-        if (e < E) {
-            int c = s_off[e] + rowv[i];
-#pragma unroll
-            for (int q = 0; q < kDispWaves; ++q) {
-                const int v = s_cur[q * E + e];
-                s_cur[q * E + e] = c;
-                c += v;
-            }
-        }
-    }
-    __syncthreads();
     // expert ids need nb bits; the all-ones pattern of nb bits is >= E and
     // tags dropped or absent assignments
+    int32_t* cur = s_cnt + wv * E;
     const int nb = 32 - __clz(E);
     const uint32_t none = (1u << nb) - 1u;
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
-        const int64_t a = a0 + (int64_t)j * kWave;
+        const int l = l0 + j * kWave;
+        const int64_t a = blk0 + l;
         const int32_t id = idv[j];
         const bool ok = valid_id(id, E);
         const uint32_t key = ok ? static_cast<uint32_t>(id) : none;
@@ -349,14 +409,22 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         const int size = __popcll(same);
         if (ok) {
             const int32_t start = cur[id];
-            const int32_t p = start + rank;
-            gather[p] = static_cast<int32_t>(a);
-            scatter[a] = p;
-            if (sorted_w) sorted_w[p] = wv8[j];
+            const int32_t s = start + rank;  // block slot
+            scatter[a] = s_gb[id] + s;
+            s_slot[s] = (id << kLocalBits) | l;
+            s_slot_w[s] = wv8[j];
             if (rank == size - 1) cur[id] = start + size;  // one writer per expert
         } else if (a < n) {
             scatter[a] = -1;
         }
+    }
+    __syncthreads();
+    // the block's slots in order: each expert's run lands contiguously
+    for (int s = t; s < nblk; s += kDispThreads) {
+        const int32_t v = s_slot[s];
+        const int32_t p = s_gb[v >> kLocalBits] + s;
+        gather[p] = static_cast<int32_t>(blk0 + (v & (kBlockChunk - 1)));
+        if (sorted_w) sorted_w[p] = s_slot_w[s];
     }
 }
 
@@ -396,14 +464,11 @@ route_status_t launch_dispatch(const DispatchProblem& d) {
                         C <= kCoarseRowsPerLane * G &&
                         (reinterpret_cast<uintptr_t>(cnt) & 15u) == 0;
     if (coarse) {
-        // place LDS: offsets, carries, and the larger of the per-wave counts
-        // and the coarse partials (2 G E + E)
-        const size_t cur_ints = std::max<size_t>((size_t)kDispWaves * d.E, (size_t)(2 * G + 1) * d.E);
         hipLaunchKernelGGL((dispatch_hist_kernel<kCoarseThreads, kCoarsePer>), dim3(C),
                            dim3(kCoarseThreads), sizeof(int32_t) * d.E, d.stream, d.ids, d.n,
                            d.E, cnt);
         hipLaunchKernelGGL(dispatch_place_kernel<true>, dim3(B), dim3(kDispThreads),
-                           sizeof(int32_t) * (place_cur_offset(d.E) + cur_ints), d.stream, d.ids,
+                           sizeof(int32_t) * place_lds(d.E, G).ints, d.stream, d.ids,
                            d.weights, d.n, d.E, cnt, nullptr, C, d.counts, d.offsets, d.gather,
                            d.scatter, d.sorted_weights);
         return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
@@ -417,7 +482,7 @@ route_status_t launch_dispatch(const DispatchProblem& d) {
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3((d.E + kWave - 1) / kWave), dim3(kScanThreads),
                        0, d.stream, d.E, B, cnt, totals);
     hipLaunchKernelGGL(dispatch_place_kernel<false>, dim3(B > 0 ? B : 1), dim3(kDispThreads),
-                       sizeof(int32_t) * (place_cur_offset(d.E) + kDispWaves * d.E), d.stream,
+                       sizeof(int32_t) * place_lds(d.E, 0).ints, d.stream,
                        d.ids, d.weights, d.n, d.E, cnt, totals, B, d.counts, d.offsets,
                        d.gather, d.scatter, d.sorted_weights);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
