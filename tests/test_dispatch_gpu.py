@@ -40,6 +40,7 @@ def _compare(ids_np, E, w_np=None, workspace=None):
     (98000, 8, 160, 0, 160, 8),  # two kernels: 96 coarse rows, every reducing thread's last
     (40000, 8, 384, -1, 385, 10),  # two kernels: 40 coarse rows over 5 reducing groups
     (65536, 8, 252, 0, 252, 11), # two kernels: 64 coarse rows of 63 quads (not a power of 2)
+    (20000, 8, 1024, -3, 1030, 12),  # three kernels at the widest expert range (79 blocks)
 ])
 def test_dispatch_random_ids(M, K, E, lo, hi, seed):
     rng = np.random.default_rng(seed)
@@ -60,6 +61,18 @@ def test_dispatch_of_full_size_routing_output():
     torch.cuda.synchronize()
     c, o, g, s, sw = _compare(ids.cpu().numpy(), wl.E, w.cpu().numpy())
     assert int(c.sum()) == 65536 * 8
+
+
+def test_dispatch_skewed_experts():
+    """A few experts take most assignments (Zipf-like ranks), so a block's
+    runs range from hundreds of entries to none, on both launch paths."""
+    rng = np.random.default_rng(13)
+    for M, E in ((65536, 256), (30000, 1024)):
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        ids = rng.choice(E, size=(M, 8), p=p / p.sum()).astype(np.int32)
+        w = rng.random((M, 8), dtype=np.float32)
+        log(f"[gpu] dispatch skewed ids M={M} E={E}")
+        _compare(ids, E, w)
 
 
 def test_dispatch_all_to_one_expert():
