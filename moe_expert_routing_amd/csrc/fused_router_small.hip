@@ -552,33 +552,34 @@ __global__ __launch_bounds__(kSmThreads) void small_router_ring_kernel(
     // loaded first: the waits of the W loads below then cover it, and no
     // wait for it is left inside the loop (one there would drain the ring).
     const float bj = BIAS && i16 < E ? bias_at(bias, i16) : 0.0f;
-    issue(0, 0);
-
     // W into registers: wf[i] holds fragment wv + 8 i (units 32 (wv + 8 i)
     // ..), built through a per-wave LDS image of 32 rows x 16 experts in the
-    // last ring stage, which the first copies do not use.
-    bf16x8 wf[FM];
+    // last ring stage, which the first copies do not use.  The first copy
+    // goes out first; then every W load of the wave is in flight at once,
+    // so that only the first image round waits (for that copy, as loads
+    // complete in issue order) and W streams at the cache's rate.
+    issue(0, 0);
+    uint4 raw[FM];
+    {
+        const int row = lane / 2, half = lane % 2;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int k = 32 * (wv + kSmWaves * i) + row;
+            raw[i] = *reinterpret_cast<const uint4*>(w + (int64_t)k * E + (E == 16 ? 8 * half : 0));
+        }
+    }
+    bf16x8 wf[FM];  // from the image rounds
     {
         unsigned char* img = ring[kRgAhead] + wv * (kSmBatch * 1024);
-        const int row = lane / 2, half = lane % 2;
+        const int half = lane % 2;
         // with 8 experts the second 16 bytes of an image row are zeros (both
         // halves load the row's 16 bytes; the second is masked)
         const uint32_t keep = E == 16 || half == 0 ? ~0u : 0u;
-        uint4 raw[2][kSmBatch];  // round rr + 1 loads while round rr is turned
-        auto wload = [&](int rr, uint4 (&dst)[kSmBatch]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < kSmBatch; ++i) {
-                const int k = 32 * (wv + kSmWaves * (kSmBatch * rr + i)) + row;
-                dst[i] = *reinterpret_cast<const uint4*>(w + (int64_t)k * E + (E == 16 ? 8 * half : 0));
-            }
-        };
-        wload(0, raw[0]);
 #pragma unroll
         for (int rr = 0; rr < FM / kSmBatch; ++rr) {
-            if (rr + 1 < FM / kSmBatch) wload(rr + 1, raw[(rr + 1) % 2]);
 #pragma unroll
             for (int i = 0; i < kSmBatch; ++i) {
-                const uint4 v = raw[rr % 2][i];
+                const uint4 v = raw[kSmBatch * rr + i];
                 *reinterpret_cast<uint4*>(img + 1024 * i + 16 * lane) =
                     make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
             }
