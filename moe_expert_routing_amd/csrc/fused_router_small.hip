@@ -261,10 +261,12 @@ route_status_t launch_sr(const FusedProblem& f) {
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
 }
 
-// One token's routing over 16 consecutive lanes: lane j holds expert j's
-// logit x (cap applied); lanes j >= E hold none.  Same rule as route_token:
-// K rounds of a butterfly argmax by (c desc, index asc), weights s of the
-// picks added in pick order; the pick of rank k is stored by its lane.
+// One token's routing over 16 consecutive lanes (one DPP row): lane j holds
+// expert j's logit x (cap applied); lanes j >= E hold none.  Same rule as
+// route_token: K rounds of an argmax by (c desc, index asc); the weights s
+// of the picks are then added across the row, and the pick of rank k is
+// stored by its lane.  Every reduction is a DPP butterfly within the row
+// (no LDS permutes), so every lane of the row holds the same bits.
 template <int E, bool SOFTMAX, bool BIAS>
 __device__ __forceinline__ void route_lanes16_b(float x, int j, bool store, float bj, int K,
                                                 int renorm, float* __restrict__ w_row,
@@ -272,33 +274,24 @@ __device__ __forceinline__ void route_lanes16_b(float x, int j, bool store, floa
     const bool live = j < E;
     float s;
     if constexpr (SOFTMAX) {
-        float mx = live ? x : -INFINITY;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+        const float mx = row_max<16>(live ? x : -INFINITY);
         const float u = live ? fast_exp2((x - mx) * kLog2e) : 0.f;
-        float sum = u;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) sum += shfl_xor(sum, o);
-        s = u / sum;
+        s = u / row_sum<16>(u);
     } else {
         s = sigmoid_f32(x);
     }
     const float c = BIAS && live ? s + bj : s;
+    // K rounds of a 16-lane arg-max (value desc, index asc) on DPP; the
+    // picked lanes' unbiased scores are summed once at the end
     bool open = live;  // not picked yet
     int rank = -1;
-    float tot = 0.f;
     for (int k = 0; k < K; ++k) {
-        float bv = open ? c : -INFINITY, bs = s;
+        float bv = open ? c : -INFINITY;
         int bi = open ? j : 0x7fffffff;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-            const float ov = shfl_xor(bv, o), os = shfl_xor(bs, o);
-            const int oi = shfl_xor(bi, o);
-            if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; bs = os; }
-        }
+        row_argmax<16>(bv, bi);
         if (bi == j) { rank = k; open = false; }
-        tot += bs;
     }
+    const float tot = row_sum<16>(rank >= 0 ? s : 0.f);
     if (store && rank >= 0) {
         w_row[rank] = renorm ? s / tot : s;
         id_row[rank] = j;

@@ -9,77 +9,6 @@
 
 namespace moe_route {
 
-constexpr int kDppXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kDppXor3 = 0x1B;     // quad_perm [3,2,1,0]
-constexpr int kDppMirror8 = 0x141; // row_half_mirror: lane i <-> 7 - i within 8
-constexpr int kDppRowMirror = 0x140;  // row_mirror: lane i <-> 15 - i within 16
-constexpr int kDppRowShl1 = 0x101;    // row_shl:1: lane i reads lane i + 1 within 16
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-// A plain DPP move for values that are compared rather than combined (the
-// form above folds into the combining instruction; this one needs no zeroed
-// old value).  Every control used here (quad_perm, row_half_mirror) reads a
-// lane of the same row for every lane, so no lane keeps an old value.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov_u32(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
-}
-
-// Reductions over the LPR lanes of a row; every lane of the row gets the
-// same bits (xor/mirror butterflies combine the same operands in each lane).
-template <int LPR>
-__device__ __forceinline__ float row_max(float v) {
-    if (LPR >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
-    if (LPR >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
-    if (LPR >= 8) v = fmaxf(v, dpp_f32<kDppMirror8>(v));
-    return v;
-}
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-    if (LPR >= 2) v = v + dpp_f32<kDppXor1>(v);
-    if (LPR >= 4) v = v + dpp_f32<kDppXor2>(v);
-    if (LPR >= 8) v = v + dpp_f32<kDppMirror8>(v);
-    return v;
-}
-template <int LPR>
-__device__ __forceinline__ float row_min(float v) {
-    if (LPR >= 2) v = fminf(v, dpp_f32<kDppXor1>(v));
-    if (LPR >= 4) v = fminf(v, dpp_f32<kDppXor2>(v));
-    if (LPR >= 8) v = fminf(v, dpp_f32<kDppMirror8>(v));
-    return v;
-}
-template <int LPR>
-__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
-    if (LPR >= 2) v = max(v, dpp_u32<kDppXor1>(v));
-    if (LPR >= 4) v = max(v, dpp_u32<kDppXor2>(v));
-    if (LPR >= 8) v = max(v, dpp_u32<kDppMirror8>(v));
-    return v;
-}
-// Row argmax over (value desc, index asc) pairs.
-template <int LPR>
-__device__ __forceinline__ void row_argmax(float& v, int& i) {
-#define MOE_ROUTE_ARGMAX_STEP(CTRL)                                   \
-    {                                                                 \
-        float ov = dpp_f32<CTRL>(v);                                  \
-        int oi = static_cast<int>(dpp_u32<CTRL>(static_cast<uint32_t>(i))); \
-        if (beats(ov, oi, v, i)) { v = ov; i = oi; }                  \
-    }
-    if (LPR >= 2) MOE_ROUTE_ARGMAX_STEP(kDppXor1)
-    if (LPR >= 4) MOE_ROUTE_ARGMAX_STEP(kDppXor2)
-    if (LPR >= 8) MOE_ROUTE_ARGMAX_STEP(kDppMirror8)
-#undef MOE_ROUTE_ARGMAX_STEP
-}
-
 // Whole-wave min / max (all lanes hold the result), on the VALU: DPP within
 // each row of 16 lanes, then the four row results through SGPRs.
 __device__ __forceinline__ float lane_f32(float v, int l) {
