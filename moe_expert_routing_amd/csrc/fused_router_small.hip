@@ -194,8 +194,7 @@ __global__ __launch_bounds__(kSrThreads) void small_router_kernel(
                 const float4 d = *reinterpret_cast<const float4*>(&red[j][32 * cb + 4 * i]);
                 v += (d.x + d.y) + (d.z + d.w);
             }
-#pragma unroll
-            for (int x = TPO / 2; x > 0; x >>= 1) v += shfl_xor(v, x);
+            v = row_sum<TPO>(v);  // the output's TPO lanes, on DPP
             if (q == 0) {
                 const int vi = 32 * r + j;  // token vi / 8, expert 8 s + vi % 8
                 logit[(vi / 8) * E + 8 * s + vi % 8] = cap != 0.0f ? cap * tanh_f32(v / cap) : v;
