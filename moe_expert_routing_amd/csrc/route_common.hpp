@@ -167,6 +167,22 @@ __device__ __forceinline__ void row_argmax(float& v, int& i) {
 #undef MOE_ROUTE_ARGMAX_STEP
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2,
+// 4 and 8 lanes within each row of 16 (lanes without a source add the zero
+// old value), then each row's total carried into the next rows by the
+// row_bcast:15 and row_bcast:31 broadcasts (GFX9 DPP).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);  // rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);  // rows 2, 3
+    return x;
+}
+
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, kWave);

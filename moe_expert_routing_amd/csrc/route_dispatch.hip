@@ -330,16 +330,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         sum_t += tot[i];
         sum_b += bc[i];
     }
-    int inc_t = sum_t, inc_b = sum_b;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int vt = __shfl_up(inc_t, o, kWave);
-        const int vb = __shfl_up(inc_b, o, kWave);
-        if (lane >= o) {
-            inc_t += vt;
-            inc_b += vb;
-        }
-    }
+    const int inc_t = wave_incl_scan(sum_t), inc_b = wave_incl_scan(sum_b);
     if (lane == kWave - 1) {
         s_wsum[wv] = inc_t;
         s_wsum[kDispWaves + wv] = inc_b;
