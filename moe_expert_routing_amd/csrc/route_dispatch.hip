@@ -10,12 +10,13 @@
 //
 // Up to 16384 counts in a coarse matrix (the usual case: 65536 tokens x 8
 // slots over 256 experts), two kernels on the caller's stream:
-//   1. hist:  one count row per 8192 assignments, cnt[C][E];
+//   1. hist:  one count row per 8192 assignments, cnt[C][E], and for each
+//             place block after the first of a row, the counts of the row's
+//             2048-assignment chunks before it (a prefix row);
 //   2. place: as in 3. below, except that each block first reduces the whole
 //             coarse matrix itself (its rows before the block's own row give
 //             the counts of earlier blocks, all rows the expert totals) and
-//             recounts the at most three 2048-assignment chunks of its own
-//             row that precede it.
+//             adds its prefix row.
 // Otherwise three kernels, with a caller-provided workspace cnt[B][E] +
 // totals[E] (B = blocks of kBlockChunk assignments):
 //   1. hist:  each block counts its chunk per expert (LDS atomics) into its
@@ -98,6 +99,50 @@ __global__ __launch_bounds__(THREADS) void dispatch_hist_kernel(
     for (int e = t; e < E; e += THREADS) cnt[(int64_t)blockIdx.x * E + e] = s_hist[e];
 }
 
+// Row of the coarse workspace that holds, for place block kSubPerRow c + s
+// (s >= 1), the counts of coarse row c's chunks before it.  The C coarse
+// rows come first; rows exist only for place blocks that exist, so the B
+// place blocks need B rows in all.
+__host__ __device__ constexpr int64_t coarse_prefix_row(int C, int c, int s) {
+    return (int64_t)C + (int64_t)(kSubPerRow - 1) * c + s - 1;
+}
+
+// Coarse row c = block x: its kCoarseChunk assignments counted per expert
+// (LDS atomics, one histogram per place-block chunk) into cnt[c][*], and for
+// each later place block of the row the counts of the chunks before it into
+// its prefix row.  B = place blocks.
+__global__ __launch_bounds__(kCoarseThreads) void dispatch_hist_coarse_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int C, int B, int32_t* __restrict__ cnt) {
+    extern __shared__ int32_t s_hist[];  // [kSubPerRow][E]
+    constexpr int kPerChunk = kBlockChunk / kCoarseThreads;  // loads of a thread per chunk
+    static_assert(kBlockChunk % kCoarseThreads == 0 && kCoarsePer == kSubPerRow * kPerChunk,
+                  "a thread's loads j fall in chunk j / kPerChunk");
+    const int t = threadIdx.x;
+    const int c = blockIdx.x;
+    const int64_t a0 = (int64_t)c * kCoarseChunk + t;
+    int32_t idv[kCoarsePer];  // all loads in flight at once
+#pragma unroll
+    for (int j = 0; j < kCoarsePer; ++j) {
+        const int64_t a = a0 + (int64_t)j * kCoarseThreads;
+        idv[j] = a < n ? ids[a] : -1;
+    }
+    for (int i = t; i < kSubPerRow * E; i += kCoarseThreads) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCoarsePer; ++j)
+        if (valid_id(idv[j], E)) atomicAdd(&s_hist[(j / kPerChunk) * E + idv[j]], 1);
+    __syncthreads();
+    for (int e = t; e < E; e += kCoarseThreads) {
+        int run = 0;
+#pragma unroll
+        for (int sb = 0; sb < kSubPerRow; ++sb) {
+            if (sb > 0 && kSubPerRow * c + sb < B) cnt[coarse_prefix_row(C, c, sb) * E + e] = run;
+            run += s_hist[sb * E + e];
+        }
+        cnt[(int64_t)c * E + e] = run;
+    }
+}
+
 // Block x, thread t: expert e = 64 x + t % 64 over segment t / 64 of the
 // block rows.  Segments combine in LDS; each column is rewritten as exclusive
 // offsets across blocks and the expert's total is written.
@@ -165,11 +210,11 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 // LDS layout of the place kernel, in ints: expert offsets [E + 1], scan
 // carries [2 kDispWaves], per-expert global bases [E]; then, 16-byte
 // aligned, the per-wave counts and cursors [kDispWaves][E], and a region
-// that first holds the coarse partials [2 G][E] and the recount [E] (COARSE)
-// and afterwards the block's assignments in sorted order [kBlockChunk] and
-// their weights [kBlockChunk].  At most 60 KiB (E = 1024).
+// that first holds the coarse partials [2 G][E] (COARSE) and afterwards the
+// block's assignments in sorted order [kBlockChunk] and their weights
+// [kBlockChunk].  At most 56 KiB (E = 1024).
 struct PlaceLds {
-    int off, wsum, gb, cnt, slot, slot_w, pre, all, rc, ints;
+    int off, wsum, gb, cnt, slot, slot_w, pre, all, ints;
 };
 __host__ __device__ constexpr PlaceLds place_lds(int E, int G) {
     PlaceLds l{};
@@ -181,8 +226,7 @@ __host__ __device__ constexpr PlaceLds place_lds(int E, int G) {
     l.slot_w = l.slot + kBlockChunk;
     l.pre = l.slot;
     l.all = l.pre + G * E;
-    l.rc = l.all + G * E;
-    const int tail = G > 0 ? 2 * G * E + E : 0;
+    const int tail = 2 * G * E;
     l.ints = l.slot + (tail > 2 * kBlockChunk ? tail : 2 * kBlockChunk);
     return l;
 }
@@ -233,11 +277,11 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
     if constexpr (COARSE) {
         // Thread t < Q * G reduces 16-byte quad q = t % Q of rows
         // r = g, g + G, ... (g = t / Q) into a before-my-row and an all-rows
-        // partial; the G partials of an expert are added in LDS.  The
-        // assignments of the preceding chunks of this block's coarse row are
-        // recounted into s_rc.
+        // partial; the G partials of an expert are added in LDS.  The counts
+        // of the chunks of this block's coarse row before it come from the
+        // row's prefix rows, written by the histogram kernel.
         const int Q = E / 4;
-        const int c = blockIdx.x / kSubPerRow;
+        const int c = blockIdx.x / kSubPerRow, sb = blockIdx.x % kSubPerRow;
         const int q = t % Q, g = t / Q;
         int4 m[kCoarseRowsPerLane];
 #pragma unroll
@@ -247,20 +291,15 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
                        ? reinterpret_cast<const int4*>(cnt + (int64_t)r * E)[q]
                        : make_int4(0, 0, 0, 0);
         }
-        const int64_t rc0 = (int64_t)c * kCoarseChunk;
-        const int nrc = (blockIdx.x % kSubPerRow) * kBlockChunk;  // assignments to recount
-        int32_t rid[kSubPerRow - 1][kPerLane];
+        int sub[kEPT];
+        const int32_t* srow = cnt + (int64_t)coarse_prefix_row(C, c, sb) * E;
 #pragma unroll
-        for (int u = 0; u < kSubPerRow - 1; ++u)
-#pragma unroll
-            for (int j = 0; j < kPerLane; ++j) {
-                const int o = (u * kPerLane + j) * kDispThreads + t;
-                rid[u][j] = o < nrc ? ids[rc0 + o] : -1;  // rc0 + o < n: earlier chunks are full
-            }
+        for (int i = 0; i < kEPT; ++i) {
+            const int e = kEPT * t + i;
+            sub[i] = sb > 0 && e < E ? srow[e] : 0;
+        }
         int32_t* s_pre = smem + L.pre;  // [G][E] partials (rows before c)
         int32_t* s_all = smem + L.all;  // [G][E] partials (all rows)
-        int32_t* s_rc = smem + L.rc;    // [E] recount
-        for (int e = t; e < E; e += kDispThreads) s_rc[e] = 0;
         if (g < G) {
             int4 pre = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
 #pragma unroll
@@ -273,24 +312,18 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < kSubPerRow - 1; ++u)
-#pragma unroll
-            for (int j = 0; j < kPerLane; ++j)
-                if (valid_id(rid[u][j], E)) atomicAdd(&s_rc[rid[u][j]], 1);
-#pragma unroll
         for (int j = 0; j < kPerLane; ++j)
             if (valid_id(idv[j], E)) atomicAdd(&s_cnt[wv * E + idv[j]], 1);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kEPT; ++i) {
             const int e = kEPT * t + i;
-            int p = 0, a = 0;
+            int p = sub[i], a = 0;
             if (e < E) {
                 for (int gg = 0; gg < G; ++gg) {
                     p += s_pre[gg * E + e];
                     a += s_all[gg * E + e];
                 }
-                p += s_rc[e];
             }
             tot[i] = a;
             rowv[i] = p;
@@ -455,9 +488,9 @@ route_status_t launch_dispatch(const DispatchProblem& d) {
                         C <= kCoarseRowsPerLane * G &&
                         (reinterpret_cast<uintptr_t>(cnt) & 15u) == 0;
     if (coarse) {
-        hipLaunchKernelGGL((dispatch_hist_kernel<kCoarseThreads, kCoarsePer>), dim3(C),
-                           dim3(kCoarseThreads), sizeof(int32_t) * d.E, d.stream, d.ids, d.n,
-                           d.E, cnt);
+        hipLaunchKernelGGL(dispatch_hist_coarse_kernel, dim3(C), dim3(kCoarseThreads),
+                           sizeof(int32_t) * kSubPerRow * d.E, d.stream, d.ids, d.n, d.E, C, B,
+                           cnt);
         hipLaunchKernelGGL(dispatch_place_kernel<true>, dim3(B), dim3(kDispThreads),
                            sizeof(int32_t) * place_lds(d.E, G).ints, d.stream, d.ids,
                            d.weights, d.n, d.E, cnt, nullptr, C, d.counts, d.offsets, d.gather,
