@@ -237,8 +237,9 @@ static_assert(kBlockChunk == 1 << kLocalBits, "block-local index width");
 static_assert(kMaxExperts << kLocalBits <= 0x7fffffff, "expert and local index in one int");
 
 // COARSE: cnt is the coarse matrix [C][E] (E a multiple of 4, 16-byte
-// aligned rows, C * E <= kCoarseMaxInts) and totals is unused; otherwise cnt
-// holds the scanned rows [B][E] and totals the expert totals.
+// aligned rows, C * E <= kCoarseMaxInts) followed by the prefix rows of
+// dispatch_hist_coarse_kernel, and totals is unused; otherwise cnt holds the
+// scanned rows [B][E] and totals the expert totals.
 template <bool COARSE>
 __global__ __launch_bounds__(kDispThreads) void dispatch_place_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t n, int E,
