@@ -123,6 +123,7 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // combine the same operands in each lane).
 template <int LPR>
 __device__ __forceinline__ float row_max(float v) {
+    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "row width");
     if (LPR >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
     if (LPR >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
     if (LPR >= 8) v = fmaxf(v, dpp_f32<kDppMirror8>(v));
@@ -142,6 +143,7 @@ __device__ __forceinline__ float row_min(float v) {
     if (LPR >= 2) v = fminf(v, dpp_f32<kDppXor1>(v));
     if (LPR >= 4) v = fminf(v, dpp_f32<kDppXor2>(v));
     if (LPR >= 8) v = fminf(v, dpp_f32<kDppMirror8>(v));
+    if (LPR >= 16) v = fminf(v, dpp_f32<kDppRowMirror>(v));
     return v;
 }
 template <int LPR>
@@ -149,6 +151,7 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
     if (LPR >= 2) v = max(v, dpp_u32<kDppXor1>(v));
     if (LPR >= 4) v = max(v, dpp_u32<kDppXor2>(v));
     if (LPR >= 8) v = max(v, dpp_u32<kDppMirror8>(v));
+    if (LPR >= 16) v = max(v, dpp_u32<kDppRowMirror>(v));
     return v;
 }
 // Row argmax over (value desc, index asc) pairs.
@@ -183,32 +186,38 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-template <typename T>
-__device__ __forceinline__ T shfl_xor(T v, int mask) {
-    return __shfl_xor(v, mask, kWave);
+// Whole-wave reductions (every lane holds the same result), on the VALU: DPP
+// within each row of 16 lanes, then the four row results through SGPRs, added
+// or compared in a fixed order.
+__device__ __forceinline__ float lane_f32(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_min_all(float v) {
+    v = row_min<16>(v);
+    return fminf(fminf(lane_f32(v, 0), lane_f32(v, 16)), fminf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_max_all(float v) {
+    v = row_max<16>(v);
+    return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, shfl_xor(v, o));
-    return v;
+__device__ __forceinline__ float wave_sum_all(float v) {
+    v = row_sum<16>(v);
+    return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
-
-// Sum over the wave; every lane receives lane 0's total so that all lanes use
-// the very same value.
-__device__ __forceinline__ float wave_sum(float v) {
+// Arg-max over the wave by (value desc, index asc).
+__device__ __forceinline__ void wave_argmax_all(float& v, int& i) {
+    row_argmax<16>(v, i);
+    float bv = lane_f32(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += shfl_xor(v, o);
-    return __shfl(v, 0, kWave);
-}
-
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        float ov = shfl_xor(v, o);
-        int oi = shfl_xor(i, o);
-        if (beats(ov, oi, v, i)) { v = ov; i = oi; }
+    for (int r = 1; r < 4; ++r) {
+        const float ov = lane_f32(v, 16 * r);
+        const int oi = __builtin_amdgcn_readlane(i, 16 * r);
+        if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
+    v = bv;
+    i = bi;
 }
 
 }  // namespace moe_route

@@ -50,14 +50,14 @@ __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
         if (SOFTMAX) {
             float mx = -INFINITY;
             for (int e = lane; e < E; e += kWave) mx = fmaxf(mx, load_logit(xr, e));
-            mx = __shfl(wave_max(mx), 0, kWave);
+            mx = wave_max_all(mx);
             float sum = 0.f;
             for (int e = lane; e < E; e += kWave) {
                 float u = fast_exp2((load_logit(xr, e) - mx) * kLog2e);
                 sc[e] = u;
                 sum += u;
             }
-            sum = wave_sum(sum);
+            sum = wave_sum_all(sum);
             for (int e = lane; e < E; e += kWave) {
                 float s = sc[e] / sum;
                 sc[e] = s;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
                 float v = ch[e];
                 if (beats(v, e, bv, bi)) { bv = v; bi = e; }
             }
-            wave_argmax(bv, bi);
+            wave_argmax_all(bv, bi);
             // bi keeps its sentinel only when no candidate beats -inf (NaN
             // scores): the output is then unspecified, but stays inside the row
             bi = min(max(bi, 0), E - 1);
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
         }
 
         // ---- weights: unbiased scores, optionally renormalised
-        float tot = wave_sum(lane < K ? my_w : 0.f);
+        float tot = wave_sum_all(lane < K ? my_w : 0.f);
         if (lane < K) {
             w_out[row * K + lane] = renorm ? my_w / tot : my_w;
             id_out[row * K + lane] = my_id;

@@ -9,22 +9,6 @@
 
 namespace moe_route {
 
-// Whole-wave min / max (all lanes hold the result), on the VALU: DPP within
-// each row of 16 lanes, then the four row results through SGPRs.
-__device__ __forceinline__ float lane_f32(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-__device__ __forceinline__ float wave_min_all(float v) {
-    v = row_min<8>(v);
-    v = fminf(v, dpp_f32<kDppRowMirror>(v));
-    return fminf(fminf(lane_f32(v, 0), lane_f32(v, 16)), fminf(lane_f32(v, 32), lane_f32(v, 48)));
-}
-__device__ __forceinline__ float wave_max_all(float v) {
-    v = row_max<8>(v);
-    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
-}
-
 template <typename T>
 __device__ __forceinline__ float load_one(const T* p, int i);
 template <>
