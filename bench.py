@@ -405,17 +405,23 @@ def measure_all(out_path=None):
     ws = torch.empty(mr.route_dispatch_workspace_size(wl.M, wl.K, wl.E), dtype=torch.uint8,
                      device=dev)
 
-    def launch_disp(i):
-        mr.route_dispatch_metadata(ids_sets[i], wl.E, w_sets[i], workspace=ws, stream=stream)
-    per_call, kern = time_calls(launch_disp, n_sets, stream, steps=200, warmup=20)
     n = wl.M * wl.K
+    outs = [(torch.empty(wl.E, dtype=torch.int32, device=dev),
+             torch.empty(wl.E + 1, dtype=torch.int32, device=dev),
+             torch.empty(n, dtype=torch.int32, device=dev),
+             torch.empty(n, dtype=torch.int32, device=dev),
+             torch.empty(n, dtype=torch.float32, device=dev)) for _ in range(n_sets)]
+
+    def launch_disp(i):
+        mr.route_dispatch_metadata(ids_sets[i], wl.E, w_sets[i], workspace=ws, stream=stream,
+                                   out=outs[i])
+    per_call, kern = time_calls(launch_disp, n_sets, stream, steps=200, warmup=20)
     nbytes = 2 * n * 4 + n * 4 + 3 * n * 4 + 2 * wl.E * 4  # ids twice, weights; 3 outputs
     r = {"workload": "dispatch_metadata_e256_m65536", "entry": "route_dispatch_metadata",
          "M": wl.M, "K": wl.K, "E": wl.E, "rotating_sets": n_sets, "us_per_call": per_call,
          "kernel_us": kern, "alg_bytes": nbytes, "GBps_kernel": nbytes / (kern * 1e-6) / 1e9,
          "note": "two kernels per call at this size (three when the coarse count matrix "
-                 "exceeds 16384 counts); us_per_call includes the library's allocations "
-                 "of the outputs in the Python binding"}
+                 "exceeds 16384 counts); outputs and workspace preallocated"}
     results.append(r)
     eprint(json.dumps(r))
     # post-routing steps on the 65536 x 8 routing output (in place)

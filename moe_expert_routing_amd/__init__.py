@@ -250,14 +250,16 @@ def route_dispatch_workspace_size(num_tokens, top_k, num_experts) -> int:
 
 
 def route_dispatch_metadata(topk_ids, num_experts, topk_weights=None, workspace=None,
-                            stream=None):
+                            stream=None, out=None):
     """Expert-sorted dispatch metadata of a routing result: the assignments
     a = token * top_k + slot in order of expert id (stable), ids outside
     [0, num_experts) dropped.  Returns (expert_counts [E], expert_offsets
     [E+1], gather_idx [M*K], scatter_idx [M*K], sorted_weights [M*K] or None),
     all int32 / float32 tensors on the ids' device.  `workspace` (a uint8
     tensor of at least route_dispatch_workspace_size bytes) is allocated when
-    not given."""
+    not given; so are the outputs unless `out` holds those five tensors
+    (sorted_weights None when topk_weights is None), which are then filled and
+    returned."""
     M, K = topk_ids.shape
     dev = topk_ids.device
     if topk_ids.dtype != torch.int32:
@@ -269,11 +271,25 @@ def route_dispatch_metadata(topk_ids, num_experts, topk_weights=None, workspace=
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
     _need_device(topk_ids, topk_weights, workspace)
-    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
-    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
-    gather = torch.empty(M * K, dtype=torch.int32, device=dev)
-    scatter = torch.empty(M * K, dtype=torch.int32, device=dev)
-    sw = None if topk_weights is None else torch.empty(M * K, dtype=torch.float32, device=dev)
+    if out is None:
+        counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        gather = torch.empty(M * K, dtype=torch.int32, device=dev)
+        scatter = torch.empty(M * K, dtype=torch.int32, device=dev)
+        sw = None if topk_weights is None else torch.empty(M * K, dtype=torch.float32, device=dev)
+    else:
+        counts, offsets, gather, scatter, sw = out
+        want = ((counts, torch.int32, (num_experts,)), (offsets, torch.int32, (num_experts + 1,)),
+                (gather, torch.int32, (M * K,)), (scatter, torch.int32, (M * K,)))
+        for t, dt, shape in want:
+            if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"out tensors must be contiguous {dt} of shape {shape}")
+        if (sw is None) != (topk_weights is None):
+            raise ValueError("out sorted_weights must be given exactly when topk_weights is")
+        if sw is not None and (sw.dtype != torch.float32 or tuple(sw.shape) != (M * K,)
+                               or not sw.is_contiguous()):
+            raise ValueError(f"out sorted_weights must be contiguous float32 of shape ({M * K},)")
+        _need_device(topk_ids, counts, offsets, gather, scatter, sw)
     _check(lib().route_dispatch_metadata(_ptr(topk_ids), _ptr(topk_weights), M, K, num_experts,
                                          _ptr(counts), _ptr(offsets), _ptr(gather),
                                          _ptr(scatter), _ptr(sw), _ptr(workspace),

@@ -82,6 +82,30 @@ def test_dispatch_all_to_one_expert():
     _compare(ids, 256, np.arange(8192 * 8, dtype=np.float32).reshape(8192, 8))
 
 
+def test_dispatch_into_given_outputs():
+    """Outputs passed in are filled and returned; they match a call that
+    allocates its own."""
+    rng = np.random.default_rng(14)
+    M, K, E = 3000, 8, 256
+    ids = torch.from_numpy(rng.integers(-1, E, size=(M, K)).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.random((M, K), dtype=np.float32)).cuda()
+    out = (torch.full((E,), 7, dtype=torch.int32, device="cuda"),
+           torch.full((E + 1,), 7, dtype=torch.int32, device="cuda"),
+           torch.full((M * K,), 7, dtype=torch.int32, device="cuda"),
+           torch.full((M * K,), 7, dtype=torch.int32, device="cuda"),
+           torch.full((M * K,), 7.0, dtype=torch.float32, device="cuda"))
+    log("[gpu] dispatch into given outputs M=3000 K=8 E=256")
+    got = mr.route_dispatch_metadata(ids, E, w, out=out)
+    ref = mr.route_dispatch_metadata(ids, E, w)
+    torch.cuda.synchronize()
+    for g, o, r in zip(got, out, ref):
+        assert g is o and torch.equal(g, r)
+    with pytest.raises(ValueError):
+        mr.route_dispatch_metadata(ids, E, w, out=out[:4] + (None,))
+    with pytest.raises(ValueError):
+        mr.route_dispatch_metadata(ids, E, w, out=(out[0][:-1],) + out[1:])
+
+
 def test_dispatch_empty():
     ids = torch.empty((0, 8), dtype=torch.int32, device="cuda")
     c, o, g, s, sw = mr.route_dispatch_metadata(ids, 16)
