@@ -41,6 +41,9 @@ def _compare(ids_np, E, w_np=None, workspace=None):
     (40000, 8, 384, -1, 385, 10),  # two kernels: 40 coarse rows over 5 reducing groups
     (65536, 8, 252, 0, 252, 11), # two kernels: 64 coarse rows of 63 quads (not a power of 2)
     (20000, 8, 1024, -3, 1030, 12),  # three kernels at the widest expert range (79 blocks)
+    (2304, 8, 256, -1, 256, 15),  # two kernels: the last coarse row holds one place block
+    (2305, 8, 256, 0, 256, 16),   # two kernels: the last coarse row holds two, the second ragged
+    (65536, 8, 250, -2, 252, 17), # three kernels: E not a multiple of 4
 ])
 def test_dispatch_random_ids(M, K, E, lo, hi, seed):
     rng = np.random.default_rng(seed)
