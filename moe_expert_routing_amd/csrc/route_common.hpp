@@ -122,8 +122,10 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // lanes); every lane of the row gets the same bits (xor/mirror butterflies
 // combine the same operands in each lane).
 template <int LPR>
+constexpr bool row_width_ok = LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16;
+template <int LPR>
 __device__ __forceinline__ float row_max(float v) {
-    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "row width");
+    static_assert(row_width_ok<LPR>, "row width");
     if (LPR >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
     if (LPR >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
     if (LPR >= 8) v = fmaxf(v, dpp_f32<kDppMirror8>(v));
@@ -132,6 +134,7 @@ __device__ __forceinline__ float row_max(float v) {
 }
 template <int LPR>
 __device__ __forceinline__ float row_sum(float v) {
+    static_assert(row_width_ok<LPR>, "row width");
     if (LPR >= 2) v = v + dpp_f32<kDppXor1>(v);
     if (LPR >= 4) v = v + dpp_f32<kDppXor2>(v);
     if (LPR >= 8) v = v + dpp_f32<kDppMirror8>(v);
@@ -140,6 +143,7 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 template <int LPR>
 __device__ __forceinline__ float row_min(float v) {
+    static_assert(row_width_ok<LPR>, "row width");
     if (LPR >= 2) v = fminf(v, dpp_f32<kDppXor1>(v));
     if (LPR >= 4) v = fminf(v, dpp_f32<kDppXor2>(v));
     if (LPR >= 8) v = fminf(v, dpp_f32<kDppMirror8>(v));
@@ -148,6 +152,7 @@ __device__ __forceinline__ float row_min(float v) {
 }
 template <int LPR>
 __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    static_assert(row_width_ok<LPR>, "row width");
     if (LPR >= 2) v = max(v, dpp_u32<kDppXor1>(v));
     if (LPR >= 4) v = max(v, dpp_u32<kDppXor2>(v));
     if (LPR >= 8) v = max(v, dpp_u32<kDppMirror8>(v));
@@ -157,6 +162,7 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
 // Row argmax over (value desc, index asc) pairs.
 template <int LPR>
 __device__ __forceinline__ void row_argmax(float& v, int& i) {
+    static_assert(row_width_ok<LPR>, "row width");
 #define MOE_ROUTE_ARGMAX_STEP(CTRL)                                   \
     {                                                                 \
         float ov = dpp_f32<CTRL>(v);                                  \
