@@ -17,6 +17,7 @@ namespace moe_route {
 namespace {
 
 constexpr int kGenericWaves = 4;  // wavefronts per workgroup
+__host__ __device__ constexpr int generic_wave_floats(int E) { return 2 * E + kMaxGroups; }
 
 template <typename T>
 __device__ __forceinline__ float load_logit(const T* p, int i);
@@ -31,15 +32,14 @@ template <typename T, bool SOFTMAX, bool TOP2>
 __global__ __launch_bounds__(kGenericWaves* kWave) void route_generic_kernel(
     const T* __restrict__ logits, BiasRef bias, int64_t M, int E, int G,
     int TG, int K, int renorm, float* __restrict__ w_out, int32_t* __restrict__ id_out) {
-    __shared__ float s_score[kGenericWaves][kMaxExperts];   // unbiased score s
-    __shared__ float s_choice[kGenericWaves][kMaxExperts];  // selection score c
-    __shared__ float s_group[kGenericWaves][kMaxGroups];
-
+    // per wave: unbiased scores s [E], selection scores c [E], group scores
+    // [kMaxGroups], sized by E so that small expert counts fit more blocks
+    extern __shared__ float s_wave[];
     const int lane = threadIdx.x % kWave;
     const int wv = threadIdx.x / kWave;
-    float* sc = s_score[wv];
-    float* ch = s_choice[wv];
-    float* gh = s_group[wv];
+    float* sc = s_wave + (size_t)wv * generic_wave_floats(E);
+    float* ch = sc + E;
+    float* gh = ch + E;
     const int gs = E / G;
 
     for (int64_t row = (int64_t)blockIdx.x * kGenericWaves + wv; row < M;
@@ -130,7 +130,8 @@ route_status_t launch_generic_t(const RouteProblem& p) {
     int64_t blocks = (p.M + kGenericWaves - 1) / kGenericWaves;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL((route_generic_kernel<T, SOFTMAX, TOP2>), dim3((unsigned)blocks),
-                       dim3(kGenericWaves * kWave), 0, p.stream,
+                       dim3(kGenericWaves * kWave),
+                       sizeof(float) * kGenericWaves * generic_wave_floats(p.E), p.stream,
                        static_cast<const T*>(p.logits), p.bias, p.M, p.E, p.G, p.TG, p.K,
                        p.renorm ? 1 : 0, p.weights, p.ids);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
