@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_route.so")
-SOURCES = ["route_api.cpp", "route_generic.hip", "route_fast.hip", "fused_router.hip",
+SOURCES = ["route_api.cpp", "route_generic.hip", "route_fast.hip", "route_row.hip", "fused_router.hip",
            "fused_router_small.hip", "route_dispatch.hip", "route_post.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

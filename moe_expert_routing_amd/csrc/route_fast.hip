@@ -263,6 +263,7 @@ route_status_t launch_route(const RouteProblem& p) {
     const bool vec_ok = aligned16(p.logits) && ((size_t)p.E * esz) % 16 == 0 &&
                         (p.bias.p == nullptr ||
                          (reinterpret_cast<uintptr_t>(p.bias.p) % (p.bias.bf16 ? 8 : 16)) == 0);
+    if (vec_ok && route_row_supported(p)) return launch_route_row(p);
     bool handled = false;
     route_status_t st = ROUTE_OK;
     if (vec_ok) {

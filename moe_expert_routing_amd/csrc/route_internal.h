@@ -76,6 +76,15 @@ int resident_blocks(F kernel, int threads) {
 // Kernel launchers (route_kernels.hip / fused_router.hip).  They assume a
 // validated problem with M > 0 and return ROUTE_OK or ROUTE_ELAUNCH.
 route_status_t launch_route(const RouteProblem& p);
+// One wavefront per row (route_row.hip): 256 experts, sigmoid scoring, K <= 8,
+// no groups or 8 groups, up to kRowMaxTokens rows; launch_route sends such
+// problems there when their pointers allow 8-byte (bf16) or 16-byte loads.
+#ifndef MOE_ROUTE_ROW_MAX_TOKENS
+#define MOE_ROUTE_ROW_MAX_TOKENS 2048
+#endif
+constexpr int64_t kRowMaxTokens = MOE_ROUTE_ROW_MAX_TOKENS;
+bool route_row_supported(const RouteProblem& p);
+route_status_t launch_route_row(const RouteProblem& p);
 route_status_t launch_fused_router(const FusedProblem& p);
 bool fused_router_supported(const FusedProblem& p);
 bool small_router_supported(const FusedProblem& p);  // E = 8 or 16 (fused_router_small.hip)

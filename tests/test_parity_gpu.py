@@ -9,8 +9,8 @@ import moe_expert_routing_amd as mr
 import oracle
 from gpu_util import log, oracle_args, route_gpu, to_device
 from parity_check import compare
-from workloads import (BIASED_GROUPED_M_SWEEP, WORKLOADS, bf16_bits_from_f32, make_bias,
-                       make_logits, random_logits)
+from workloads import (BIASED_GROUPED_M_SWEEP, WORKLOADS, bf16_bits_from_f32,
+                       bf16_bits_to_f32, make_bias, make_logits, random_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,10 +100,17 @@ def _kernel_variants():
     return out
 
 
+# Row counts on both sides of the one-row-per-wave kernel's limit (2048
+# tokens): 256 experts with sigmoid scoring take that kernel below it and the
+# 8-row kernel above.
+SMALL_M, LARGE_M = 1000, 2500
+
+
+@pytest.mark.parametrize("M", [SMALL_M, LARGE_M])
 @pytest.mark.parametrize("entry,dtype,E,G,TG,K,scoring,with_bias", _kernel_variants())
-def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias):
+def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias, M):
     rng = np.random.default_rng(E * 100 + G * 10 + K + (1 if with_bias else 0) + len(scoring))
-    M = 1000  # ragged last tile for every layout
+    # ragged last tile for every layout
     x = random_logits(rng, M, E, dtype, std=1.5)
     b = (rng.standard_normal(E) * 0.1).astype(np.float32) if with_bias else None
     log(f"[gpu] {entry} {dtype} E={E} G={G} TG={TG} K={K} {scoring} bias={with_bias}")
@@ -114,13 +121,13 @@ def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias)
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("M", [777, 2777])
 @pytest.mark.parametrize("K", [1, 3, 5, 7])
 @pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
-def test_biased_kernel_every_k(K, G, TG):
+def test_biased_kernel_every_k(K, G, TG, M):
     """The biased kernels unroll their merge rounds to eight and leave after
     the K-th: every K below eight, grouped and ungrouped."""
     rng = np.random.default_rng(300 + 10 * K + G)
-    M = 777
     x = random_logits(rng, M, 256, "bf16", std=1.5)
     b = (rng.standard_normal(256) * 0.1).astype(np.float32)
     log(f"[gpu] route_biased_grouped_topk bf16 E=256 G={G} TG={TG} K={K} M={M}")
@@ -132,8 +139,11 @@ def test_biased_kernel_every_k(K, G, TG):
 
 
 @pytest.mark.parametrize("E,G,TG,K,dtype,M,half", [
-    (256, 8, 4, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, top-2-sum groups
-    (256, 1, 1, 8, "bf16", 1000, 3.0),   # shape-specialised kernel, ungrouped
+    (256, 8, 4, 8, "bf16", 3000, 3.0),   # 8-row kernel, top-2-sum groups
+    (256, 1, 1, 8, "bf16", 3000, 3.0),   # 8-row kernel, ungrouped
+    (256, 8, 4, 8, "bf16", 1000, 3.0),   # one row per wave, top-2-sum groups
+    (256, 1, 1, 8, "f32", 1000, 3.0),    # one row per wave, ungrouped
+    (256, 8, 4, 8, "bf16", 3000, 1.2),   # 8-row kernel, coarsest key window
     (160, 8, 3, 6, "f32", 777, 3.0),     # 160 experts in groups of 20
     (384, 8, 4, 8, "bf16", 300, 3.0),    # generic kernel
     (256, 8, 4, 8, "bf16", 1000, 1.2),   # widest window that keeps the keys (R = 4)
@@ -156,14 +166,15 @@ def test_wide_bias_takes_the_exact_path(E, G, TG, K, dtype, M, half):
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("M", [512, 2560])
 @pytest.mark.parametrize("entry,scoring", [("route_biased_grouped_topk", "sigmoid"),
                                            ("route_grouped_topk", "softmax"),
                                            ("route_topk_softmax", "softmax")])
-def test_exact_ties_resolve_by_index(entry, scoring):
+def test_exact_ties_resolve_by_index(entry, scoring, M):
     """Logits drawn from 5 values: most scores tie exactly and the lower
     expert index must win, with no tolerance."""
     rng = np.random.default_rng(77)
-    M, E = 512, 256
+    E = 256
     G, TG, K = (1, 1, 8) if entry == "route_topk_softmax" else (8, 4, 8)
     x = bf16_bits_from_f32((rng.integers(-2, 3, size=(M, E)) * 0.5).astype(np.float32))
     log(f"[gpu] ties {entry} M={M} E={E}")
@@ -173,6 +184,7 @@ def test_exact_ties_resolve_by_index(entry, scoring):
     assert rep.ok() and rep.exact == M, rep.summary()
 
 
+@pytest.mark.parametrize("M", [SMALL_M, LARGE_M])
 @pytest.mark.parametrize("entry,E,G,TG,K,scoring,dtype,hot", [
     ("route_biased_grouped_topk", 256, 8, 4, 8, "sigmoid", "bf16", 16),
     ("route_grouped_topk", 256, 8, 4, 8, "sigmoid", "f32", 16),
@@ -180,13 +192,12 @@ def test_exact_ties_resolve_by_index(entry, scoring):
     ("route_topk_softmax", 256, 1, 1, 8, "softmax", "f32", 32),
     ("route_grouped_topk", 160, 8, 3, 6, "softmax", "f32", 10),
 ])
-def test_one_lane_holds_most_picks(entry, E, G, TG, K, scoring, dtype, hot):
+def test_one_lane_holds_most_picks(entry, E, G, TG, K, scoring, dtype, hot, M):
     """About half the rows have their whole top K among the first `hot`
     experts, the candidates one lane of the kernel holds: more picks than
     its short list keeps, so those waves must take the exact path.  The
     other rows are ordinary, so waves mix both kinds."""
     rng = np.random.default_rng(E * 10 + K)
-    M = 1000
     xf = rng.standard_normal((M, E), dtype=np.float32)
     hot_rows = rng.random(M) < 0.5
     xf[hot_rows, :hot] += np.float32(6.0)
@@ -255,8 +266,9 @@ def test_bad_arguments_raise_before_launch():
         mr.route_topk_softmax(x.t(), 2)                         # not contiguous
 
 
+@pytest.mark.parametrize("M", [1000, 4096])
 @pytest.mark.parametrize("logit_dtype", ["bf16", "f32"])
-def test_near_tied_picks_keep_the_exact_order(logit_dtype):
+def test_near_tied_picks_keep_the_exact_order(logit_dtype, M):
     """Pairs of experts (2j, 2j+1) whose biases differ by 3e-8 .. 6e-7 in
     favour of the higher index, given equal high logits in every row: their
     selection scores are closer than the kernel's fixed-point step, so the
@@ -264,7 +276,7 @@ def test_near_tied_picks_keep_the_exact_order(logit_dtype):
     out in the exact order (the strict rule: only the K-th pick may differ
     on a near tie, as it does where a planted pair straddles it)."""
     rng = np.random.default_rng(2024)
-    M, E, K, G, TG = 4096, 256, 8, 8, 4
+    E, K, G, TG = 256, 8, 8, 4
     base = (rng.standard_normal(E // 2) * 0.05).astype(np.float32)
     gap = rng.uniform(3e-8, 6e-7, size=E // 2)
     b = np.empty(E, np.float32)
@@ -285,3 +297,55 @@ def test_near_tied_picks_keep_the_exact_order(logit_dtype):
     log(f"[gpu]   {rep.summary()}")
     # planted pairs that straddle the K-th pick are the one allowed exception
     assert rep.strict_ok and rep.exact + rep.near_tie_k == M, rep.summary()
+
+
+def _row_kernel_cases():
+    """(dtype, bias kind, G, TG, K, entry, half-width of a uniform bias or 0)"""
+    out = []
+    for dtype in ("bf16", "f32"):
+        for bias in ("f32", "bf16", None):
+            out += [(dtype, bias, 8, 4, 8, "route_biased_grouped_topk", 0.0),
+                    (dtype, bias, 1, 1, 8, "route_biased_grouped_topk", 0.0),
+                    (dtype, bias, 8, 2, 5, "route_biased_grouped_topk", 0.0)]
+        out += [(dtype, None, 8, 3, 6, "route_grouped_topk", 0.0),
+                (dtype, "f32", 8, 4, 8, "route_biased_grouped_topk", 3.0),
+                (dtype, "f32", 1, 1, 8, "route_biased_grouped_topk", 3.0)]
+    return out
+
+
+@pytest.mark.parametrize("dtype,bias_kind,G,TG,K,entry,half", _row_kernel_cases())
+def test_row_kernel_matches_the_8_row_kernel(dtype, bias_kind, G, TG, K, entry, half):
+    """Up to 2048 tokens a row goes to the one-row-per-wave kernel, above to
+    the 8-row kernel; both take the same decisions with the same arithmetic,
+    so rows routed in a batch of 2500 and again in a slice of 1500 or 7 give
+    the same bits (and the oracle's result)."""
+    rng = np.random.default_rng(len(_row_kernel_cases()) + G * 7 + TG * 3 + K + int(half))
+    M = 2500
+    x = random_logits(rng, M, 256, dtype, std=1.5)
+    b = None
+    if bias_kind is not None:
+        b = (rng.uniform(-half, half, 256) if half else rng.standard_normal(256) * 0.1
+             ).astype(np.float32)
+        if bias_kind == "bf16":
+            b = bf16_bits_to_f32(bf16_bits_from_f32(b))
+    log(f"[gpu] row kernel vs 8-row kernel {entry} {dtype} bias={bias_kind} G={G} TG={TG} "
+        f"K={K} half={half}")
+    bd = None
+    if b is not None:
+        bd = to_device(bf16_bits_from_f32(b)) if bias_kind == "bf16" else to_device(b)
+    xd = to_device(x)
+
+    def run(xs):
+        if entry == "route_grouped_topk":
+            return mr.route_grouped_topk(xs, K, G, TG, True, "sigmoid")
+        return mr.route_biased_grouped_topk(xs, bd, K, G, TG, True)
+    w_all, i_all = run(xd)
+    w_mid, i_mid = run(xd[500:2000].contiguous())
+    w_few, i_few = run(xd[1234:1241].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(w_mid, w_all[500:2000]) and torch.equal(i_mid, i_all[500:2000])
+    assert torch.equal(w_few, w_all[1234:1241]) and torch.equal(i_few, i_all[1234:1241])
+    sc, rule = oracle_args(entry, "sigmoid")
+    rep = compare(x, w_all.cpu().numpy(), i_all.cpu().numpy(), scoring=sc, bias=b, G=G, TG=TG,
+                  rule=rule, K=K, renorm=True)
+    assert rep.ok(), rep.summary()

@@ -66,7 +66,9 @@ def _f32_bias_tensor(b, offset):
 @pytest.mark.parametrize("M,E,K,G,TG,dtype,offset", [
     (65536, 256, 8, 8, 4, "bf16", 0),   # the DeepSeek-V3 shape, 65536 tokens
     (4096, 256, 8, 1, 1, "bf16", 0),    # the aiter call's ungrouped shape
-    (1000, 256, 8, 8, 4, "f32", 0),     # fp32 logits, bf16 bias
+    (1000, 256, 8, 8, 4, "f32", 0),     # fp32 logits, bf16 bias (one row per wave)
+    (3000, 256, 8, 8, 4, "f32", 0),     # fp32 logits, bf16 bias (8-row kernel)
+    (1000, 256, 8, 1, 1, "bf16", 0),    # ungrouped, one row per wave
     (1000, 256, 8, 8, 4, "bf16", 1),    # bias 2-byte aligned only: the generic kernel
     (300, 384, 8, 8, 4, "bf16", 0),     # the generic kernel
     (1000, 8, 2, 1, 1, "f32", 0),       # one lane per row (8 experts)
