@@ -60,6 +60,31 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(a, b);
 }
 
+// Smallest and largest value over the wave, in every lane: both reductions
+// at once, on integers whose signed order is the order of the floats (the
+// bits, with the magnitude bits flipped for negative values).
+__device__ __forceinline__ int float_order_key(float f) {
+    const int b = __float_as_int(f);
+    return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ void wave_min_max(float& mn, float& mx) {
+    int a = float_order_key(mn), b = float_order_key(mx);
+#define MOE_ROUTE_MINMAX_STEP(CTRL)                                            \
+    a = min(a, __builtin_amdgcn_update_dpp(0, a, CTRL, 0xF, 0xF, false));      \
+    b = max(b, __builtin_amdgcn_update_dpp(0, b, CTRL, 0xF, 0xF, false));
+    MOE_ROUTE_MINMAX_STEP(kDppXor1)
+    MOE_ROUTE_MINMAX_STEP(kDppXor2)
+    MOE_ROUTE_MINMAX_STEP(kDppMirror8)
+    MOE_ROUTE_MINMAX_STEP(kDppRowMirror)
+#undef MOE_ROUTE_MINMAX_STEP
+    a = min(min(__builtin_amdgcn_readlane(a, 0), __builtin_amdgcn_readlane(a, 16)),
+            min(__builtin_amdgcn_readlane(a, 32), __builtin_amdgcn_readlane(a, 48)));
+    b = max(max(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
+            max(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+    mn = __int_as_float(a ^ ((a >> 31) & 0x7fffffff));
+    mx = __int_as_float(b ^ ((b >> 31) & 0x7fffffff));
+}
+
 // Value of lane `src` (a lane index per lane), through the permute network.
 __device__ __forceinline__ float lane_gather(float v, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
@@ -90,22 +115,24 @@ __global__ __launch_bounds__(kRowWaves* kWave) void route_row_kernel(
     const int lane = threadIdx.x % kWave;
     const int64_t stride = (int64_t)gridDim.x * kRowWaves;
     int64_t row = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
-    if (row >= M) return;  // a whole wave; the kernel has no block barrier
 
-    // The row's logits are requested first, then the bias (4 entries a lane).
+    // The row's logits are requested first (a wave past the last row loads
+    // that row and leaves), then the bias (4 entries a lane).
     float x[4];
-    load_row4<T>(logits + row * kRowE, lane, x);
+    load_row4<T>(logits + min(row, M - 1) * kRowE, lane, x);
     float b[4] = {0.f, 0.f, 0.f, 0.f};
     KeyParams kp;
     if constexpr (BIAS) {
         const float4 bq = bias4_at(bias, lane);
         b[0] = bq.x; b[1] = bq.y; b[2] = bq.z; b[3] = bq.w;
-        const float bmin = fminf(fminf(b[0], b[1]), fminf(b[2], b[3]));
-        const float bmax = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
-        kp = key_params(wave_min_all(bmin), 1.0f + wave_max_all(bmax));
+        float bmin = fminf(fminf(b[0], b[1]), fminf(b[2], b[3]));
+        float bmax = fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]));
+        wave_min_max(bmin, bmax);
+        kp = key_params(bmin, 1.0f + bmax);
     } else {
         kp = key_params(0.0f, 1.0f);
     }
+    if (row >= M) return;  // a whole wave; the kernel has no block barrier
     float off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) off[i] = BIAS ? sel_offset(b[i], kp) : 0.0f;

@@ -69,12 +69,20 @@ struct KeyParams {
 
 // Choose the fixed-point window [lo, lo + R) that holds every selection score.
 __device__ __forceinline__ KeyParams key_params(float cmin, float cmax) {
-    float span = (cmax - cmin) * 1.001f + 1e-6f;
-    float R = 2.0f;
-    while (R < span) R *= 2.0f;
+    const float span = (cmax - cmin) * 1.001f + 1e-6f;
+    // R = 2^e, the smallest power of two >= span and at least 2: e is the
+    // exponent of span, plus one when its mantissa is not zero (a NaN span
+    // keeps R = 2; a span above 2^127 gives R = inf and scale 0)
+    int e = 1;
+    if (span > 2.0f) {
+        const uint32_t u = __float_as_uint(span);
+        e = static_cast<int>(u >> 23) - 127 + ((u & 0x7fffffu) != 0u ? 1 : 0);
+    }
+    const float R = e >= 128 ? INFINITY : __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
     float lo = cmin - R * (1.0f / 1048576.0f);  // keeps t >= 2^23 + 8
     KeyParams kp;
-    kp.scale = 8388608.0f / R;
+    // 2^23 / R, exactly
+    kp.scale = e >= 128 ? 0.0f : __uint_as_float(static_cast<uint32_t>(150 - e) << 23);
     kp.offs = 8388608.0f - lo * kp.scale;
     kp.exact_only = R > 4.0f;
     kp.sel_mul = kp.exact_only ? 1.0f : kp.scale;
