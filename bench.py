@@ -546,8 +546,14 @@ def profile_run(calls=5):
                     w, ids = out
         torch.cuda.synchronize()
         eprint(f"[profile] {name}: {calls} calls")
-    # dispatch metadata of the 65536-token routing output
+    # the 64-token case (one wavefront per row)
     wl = WORKLOADS["biased_grouped_e256"]
+    b64 = dev_tensor(make_bias(wl))
+    for x in sets(dev_tensor(make_logits(wl, 64)), calls):
+        mr.route_biased_grouped_topk(x, b64, wl.K, wl.G, wl.TG, wl.renormalize)
+    torch.cuda.synchronize()
+    eprint(f"[profile] {wl.name} M=64: {calls} calls")
+    # dispatch metadata of the 65536-token routing output
     for _ in range(calls):
         mr.route_dispatch_metadata(ids, wl.E, w)
     torch.cuda.synchronize()
