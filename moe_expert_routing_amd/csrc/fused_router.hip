@@ -34,11 +34,15 @@
 #include "route_common.hpp"
 #include "route_internal.h"
 #include "lds_copy.hpp"
+#include "route_row.hpp"
 #include "route_tile.hpp"
 
 namespace moe_route {
 namespace {
 
+#ifndef FR_WAVE_ROUTE
+#define FR_WAVE_ROUTE 1
+#endif
 constexpr int kFrRows = 32;                   // tokens per workgroup
 constexpr int kFrE = 256;                     // experts
 constexpr int kFrBK = 64;                     // hidden units per step
@@ -421,9 +425,11 @@ __global__ __launch_bounds__(kFrStepThreads) void fused_router_step_kernel(
 // Many splits (8 or more): one row per block of 1024 threads, 64 float4
 // columns x 16 split slices.  Slice q adds splits q, q + 16, ... in that
 // order and the slice sums are added in slice order; the sum is soft-capped
-// and the first wave routes the row with the fused kernel's epilogue (its
-// other 7 row slots are computed, never stored).
-template <bool SOFTMAX, bool BIAS, int GRP>
+// and the first wave routes the row: with sigmoid scoring (WAVE) by the
+// one-row-per-wave core (route_row.hpp, 4 experts a lane), otherwise with
+// the fused kernel's epilogue (its other 7 row slots computed, never
+// stored).
+template <bool SOFTMAX, bool BIAS, int GRP, bool WAVE>
 __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     const float* __restrict__ part, int64_t M, int nsplit, float cap,
     BiasRef bias, int TG, int K, int renorm, float* __restrict__ w_out,
@@ -447,7 +453,11 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     // key window (waves 0-3, which stage the bias offsets: wave i entries
     // [64 i, 64 i + 64); wave 0 routes the row)
     KeyParams kp = key_params(0.0f, 1.0f);
-    if constexpr (BIAS) {
+    float off[4];  // WAVE: the bias offsets of wave 0's lanes (4 experts each)
+    if constexpr (WAVE) {
+        static_assert(!SOFTMAX, "the one-row-per-wave core scores with sigmoid");
+        if (t < kWave) kp = row_wave_key_window<BIAS>(bias, t, off);
+    } else if constexpr (BIAS) {
         if (t < kFrE) {
             float b[4];
             kp = bias_key_params<kFrE>(bias, b);
@@ -472,6 +482,13 @@ __global__ __launch_bounds__(1024) void fr_reduce_route_kernel(
     __syncthreads();
     if (t >= kWave) return;
 
+    if constexpr (WAVE) {
+        const float4 d = reinterpret_cast<const float4*>(L)[t];
+        const float x4[4] = {d.x, d.y, d.z, d.w};
+        route_row_wave<BIAS, GRP>(x4, t, bias, off, kp, TG, K, renorm, w_out + row * K,
+                                  id_out + row * K, [&](int e) { return L[e]; });
+        return;
+    }
     const int sub = t % 8, rw = t / 8;
     float x[32];
 #pragma unroll
@@ -569,8 +586,15 @@ route_status_t launch_rr(const FusedProblem& f, const float* part, int nsplit) {
     // 8+ splits (up to 1024 tokens of a 7168-wide router): a block per row
     // sums them 16 wide; fewer splits: a wave per 8 rows, each lane adding
     // its logits over the splits
-    if (nsplit >= 8)
-        hipLaunchKernelGGL((fr_reduce_route_kernel<SOFTMAX, BIAS, GRP>), dim3((unsigned)f.M),
+    // The one-row-per-wave routing loads the bias 4 entries at a time.
+    const bool bias_4x = p.bias.p == nullptr ||
+                         reinterpret_cast<uintptr_t>(p.bias.p) % (p.bias.bf16 ? 8 : 16) == 0;
+    if (nsplit >= 8 && !SOFTMAX && bias_4x && p.K <= kRowKMax && FR_WAVE_ROUTE)
+        hipLaunchKernelGGL((fr_reduce_route_kernel<false, BIAS, GRP, true>), dim3((unsigned)f.M),
+                           dim3(1024), 0, p.stream, part, f.M, nsplit, f.softcap, p.bias, p.TG,
+                           p.K, p.renorm ? 1 : 0, p.weights, p.ids);
+    else if (nsplit >= 8)
+        hipLaunchKernelGGL((fr_reduce_route_kernel<SOFTMAX, BIAS, GRP, false>), dim3((unsigned)f.M),
                            dim3(1024), 0, p.stream, part, f.M, nsplit, f.softcap, p.bias, p.TG,
                            p.K, p.renorm ? 1 : 0, p.weights, p.ids);
     else
