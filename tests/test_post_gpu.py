@@ -105,14 +105,17 @@ def test_bf16_correction_bias(M, E, K, G, TG, dtype, offset):
     assert rep.ok(), rep.summary()
 
 
-@pytest.mark.parametrize("M,H,E,K,G,TG,workspace", [
-    (130, 512, 256, 8, 8, 4, False),    # one fused kernel
-    (130, 2048, 256, 8, 8, 4, None),    # split path: a block per row
-    (3000, 640, 256, 8, 8, 4, None),    # split path: a wave per 8 rows
-    (300, 2048, 16, 4, 1, 1, None),     # 16 experts
+@pytest.mark.parametrize("M,H,E,K,G,TG,workspace,offset", [
+    (130, 512, 256, 8, 8, 4, False, 0),    # one fused kernel
+    (130, 2048, 256, 8, 8, 4, None, 0),    # split path: a block per row, row routed by one wave
+    (130, 2048, 256, 8, 8, 4, None, 1),    # the same, bias 2-byte aligned: the 8-lane epilogue
+    (3000, 640, 256, 8, 8, 4, None, 0),    # split path: a wave per 8 rows
+    (300, 2048, 16, 4, 1, 1, None, 0),     # 16 experts
 ])
-def test_bf16_correction_bias_fused_router(M, H, E, K, G, TG, workspace):
-    """A bf16 correction bias on every fused-router path."""
+def test_bf16_correction_bias_fused_router(M, H, E, K, G, TG, workspace, offset):
+    """A bf16 correction bias on every fused-router path (a misaligned one
+    takes the epilogue that loads it entry by entry and gives the same
+    bits)."""
     rng = np.random.default_rng(M * 3 + H + E)
     hidden = bf16_bits_from_f32(rng.standard_normal((M, H), dtype=np.float32))
     wr = bf16_bits_from_f32(rng.standard_normal((H, E), dtype=np.float32) *
@@ -123,11 +126,17 @@ def test_bf16_correction_bias_fused_router(M, H, E, K, G, TG, workspace):
         f"{'one kernel' if workspace is False else 'default'}")
     hd, wd = to_device(hidden), to_device(wr)
     w, ids = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid",
-                                   _bf16_bias_tensor(bits, 0), "top2sum", workspace=workspace)
-    w2, ids2 = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid", to_device(b), "top2sum",
-                                     workspace=workspace)
+                                   _bf16_bias_tensor(bits, offset), "top2sum",
+                                   workspace=workspace)
+    w2, ids2 = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid",
+                                     _f32_bias_tensor(b, offset), "top2sum", workspace=workspace)
     torch.cuda.synchronize()
     assert torch.equal(w, w2) and torch.equal(ids, ids2)
+    if offset:
+        w3, ids3 = mr.route_fused_router(hd, wd, K, G, TG, True, "sigmoid", to_device(b),
+                                         "top2sum", workspace=workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(w, w3) and torch.equal(ids, ids3)
     logits = oracle.router_logits(hidden, wr)
     rep = compare(logits, w.cpu().numpy(), ids.cpu().numpy(), scoring=oracle.SIGMOID, bias=b,
                   G=G, TG=TG, rule=oracle.GROUP_TOP2SUM, K=K, renorm=True)
