@@ -44,6 +44,11 @@ route_status_t launch_route_generic(const RouteProblem& p);
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+#ifndef MOE_ROUTE_MID_MAX_TOKENS
+#define MOE_ROUTE_MID_MAX_TOKENS 4096
+#endif
+// Ungrouped rows of 256 experts up to this many tokens use 16 lanes a row.
+constexpr int64_t kMidMaxTokens = MOE_ROUTE_MID_MAX_TOKENS;
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left unbounded
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -97,7 +102,8 @@ __global__ __launch_bounds__(kWavesPerBlock* kWave, 3) void route_fast_kernel(
     constexpr int RPW = kWave / LPR;               // rows per wave
     static_assert(GRP == 0 || VPL % SPLIT == 0, "a group splits evenly");
     static_assert(E <= 512, "9 index bits");
-    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
+    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || (LPR == 16 && GRP == 0),
+                  "lanes per row");
     static_assert(GRP == 0 || LPR == 8, "grouped kernels hold one of 8 groups per lane");
 
     // Selection scores of the wave's rows (the candidate exchange and the
@@ -215,6 +221,15 @@ route_status_t dispatch_lpr8_k(const RouteProblem& p, bool& handled) {
     const bool soft = p.scoring == ROUTE_SOFTMAX;
     const bool bias = p.bias.p != nullptr;
     if (p.G == 1) {
+        if constexpr (VPL == 32) {
+            // up to kMidMaxTokens, 16 lanes a row: twice the waves, each
+            // with half the experts per lane
+            if (p.M <= kMidMaxTokens) {
+                if (soft) return launch_fast<T, 16, 16, true, false, 0, 1, TLU, KMAX>(p);
+                if (bias) return launch_fast<T, 16, 16, false, true, 0, 1, TLU, KMAX>(p);
+                return launch_fast<T, 16, 16, false, false, 0, 1, TLU, KMAX>(p);
+            }
+        }
         if (soft) return launch_fast<T, 8, VPL, true, false, 0, 1, TLU, KMAX>(p);
         if (bias) return launch_fast<T, 8, VPL, false, true, 0, 1, TLU, KMAX>(p);
         return launch_fast<T, 8, VPL, false, false, 0, 1, TLU, KMAX>(p);

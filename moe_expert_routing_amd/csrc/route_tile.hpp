@@ -196,7 +196,8 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
     constexpr int ROW = LPR > 1 ? E : 4;           // fp32 values per row in LDS
     static_assert(GRP == 0 || VPL % SPLIT == 0, "a group splits evenly");
     static_assert(E <= 512, "9 index bits");
-    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
+    static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8 || (LPR == 16 && GRP == 0),
+                  "lanes per row");
     static_assert(GRP == 0 || LPR == 8, "grouped kernels hold one of 8 groups per lane");
     static_assert(LPR > 1 || TL >= KMAX, "one lane per row reads its picks off its list");
     // A lane keeps only its TL best keys.  When that can be fewer than a
@@ -468,7 +469,9 @@ __device__ __forceinline__ void route_rows(float (&x)[VPL], const int sub, const
     // ties at the K-th pick itself, or between kept and dropped groups, are
     // left to the keys.)
     int slot0 = sub;  // output slot of this lane's first pick
-    if constexpr (!SOFTMAX && LPR == 8 && SLOTS == 1) {
+    // (With 16 lanes a row the K <= 8 picks sit in the first 8 lanes, and the
+    // DPP patterns below stay inside each half of the row.)
+    if constexpr (!SOFTMAX && (LPR == 8 || LPR == 16) && SLOTS == 1) {
         // keys are (value << 9 | index bits), sorted descending along the
         // row's lanes: a value gap of at most kNearKeySteps makes the key
         // difference less than (kNearKeySteps + 1) << 9 (a gap one step

@@ -100,13 +100,13 @@ def _kernel_variants():
     return out
 
 
-# Row counts on both sides of the one-row-per-wave kernel's limit (2048
-# tokens): 256 experts with sigmoid scoring take that kernel below it and the
-# 8-row kernel above.
-SMALL_M, LARGE_M = 1000, 2500
+# Row counts for each layout of 256 experts: up to 2048 tokens sigmoid
+# scoring takes the one-row-per-wave kernel; up to 4096 tokens ungrouped rows
+# take 16 lanes a row; the rest 8 lanes a row.
+SMALL_M, MID_M, LARGE_M = 1000, 3000, 5000
 
 
-@pytest.mark.parametrize("M", [SMALL_M, LARGE_M])
+@pytest.mark.parametrize("M", [SMALL_M, MID_M, LARGE_M])
 @pytest.mark.parametrize("entry,dtype,E,G,TG,K,scoring,with_bias", _kernel_variants())
 def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias, M):
     rng = np.random.default_rng(E * 100 + G * 10 + K + (1 if with_bias else 0) + len(scoring))
@@ -121,7 +121,7 @@ def test_every_specialised_kernel(entry, dtype, E, G, TG, K, scoring, with_bias,
     assert rep.ok(), rep.summary()
 
 
-@pytest.mark.parametrize("M", [777, 2777])
+@pytest.mark.parametrize("M", [777, 2777, 4777])
 @pytest.mark.parametrize("K", [1, 3, 5, 7])
 @pytest.mark.parametrize("G,TG", [(8, 4), (1, 1)])
 def test_biased_kernel_every_k(K, G, TG, M):
@@ -140,7 +140,8 @@ def test_biased_kernel_every_k(K, G, TG, M):
 
 @pytest.mark.parametrize("E,G,TG,K,dtype,M,half", [
     (256, 8, 4, 8, "bf16", 3000, 3.0),   # 8-row kernel, top-2-sum groups
-    (256, 1, 1, 8, "bf16", 3000, 3.0),   # 8-row kernel, ungrouped
+    (256, 1, 1, 8, "bf16", 3000, 3.0),   # 16 lanes a row, ungrouped
+    (256, 1, 1, 8, "bf16", 5000, 3.0),   # 8-row kernel, ungrouped
     (256, 8, 4, 8, "bf16", 1000, 3.0),   # one row per wave, top-2-sum groups
     (256, 1, 1, 8, "f32", 1000, 3.0),    # one row per wave, ungrouped
     (256, 8, 4, 8, "bf16", 3000, 1.2),   # 8-row kernel, coarsest key window
@@ -166,7 +167,7 @@ def test_wide_bias_takes_the_exact_path(E, G, TG, K, dtype, M, half):
     assert rep.ok(), rep.summary()
 
 
-@pytest.mark.parametrize("M", [512, 2560])
+@pytest.mark.parametrize("M", [512, 2560, 4600])
 @pytest.mark.parametrize("entry,scoring", [("route_biased_grouped_topk", "sigmoid"),
                                            ("route_grouped_topk", "softmax"),
                                            ("route_topk_softmax", "softmax")])
@@ -184,7 +185,7 @@ def test_exact_ties_resolve_by_index(entry, scoring, M):
     assert rep.ok() and rep.exact == M, rep.summary()
 
 
-@pytest.mark.parametrize("M", [SMALL_M, LARGE_M])
+@pytest.mark.parametrize("M", [SMALL_M, MID_M, LARGE_M])
 @pytest.mark.parametrize("entry,E,G,TG,K,scoring,dtype,hot", [
     ("route_biased_grouped_topk", 256, 8, 4, 8, "sigmoid", "bf16", 16),
     ("route_grouped_topk", 256, 8, 4, 8, "sigmoid", "f32", 16),
@@ -315,12 +316,13 @@ def _row_kernel_cases():
 
 @pytest.mark.parametrize("dtype,bias_kind,G,TG,K,entry,half", _row_kernel_cases())
 def test_row_kernel_matches_the_8_row_kernel(dtype, bias_kind, G, TG, K, entry, half):
-    """Up to 2048 tokens a row goes to the one-row-per-wave kernel, above to
-    the 8-row kernel; both take the same decisions with the same arithmetic,
-    so rows routed in a batch of 2500 and again in a slice of 1500 or 7 give
-    the same bits (and the oracle's result)."""
+    """Up to 2048 tokens a row goes to the one-row-per-wave kernel, up to 4096
+    ungrouped rows to 16 lanes a row, and otherwise to 8 lanes a row; all take
+    the same decisions with the same arithmetic, so rows routed in a batch of
+    5000 and again in slices of 3000, 1500 or 7 give the same bits (and the
+    oracle's result)."""
     rng = np.random.default_rng(len(_row_kernel_cases()) + G * 7 + TG * 3 + K + int(half))
-    M = 2500
+    M = 5000
     x = random_logits(rng, M, 256, dtype, std=1.5)
     b = None
     if bias_kind is not None:
@@ -340,9 +342,11 @@ def test_row_kernel_matches_the_8_row_kernel(dtype, bias_kind, G, TG, K, entry, 
             return mr.route_grouped_topk(xs, K, G, TG, True, "sigmoid")
         return mr.route_biased_grouped_topk(xs, bd, K, G, TG, True)
     w_all, i_all = run(xd)
+    w_3k, i_3k = run(xd[1500:4500].contiguous())
     w_mid, i_mid = run(xd[500:2000].contiguous())
     w_few, i_few = run(xd[1234:1241].contiguous())
     torch.cuda.synchronize()
+    assert torch.equal(w_3k, w_all[1500:4500]) and torch.equal(i_3k, i_all[1500:4500])
     assert torch.equal(w_mid, w_all[500:2000]) and torch.equal(i_mid, i_all[500:2000])
     assert torch.equal(w_few, w_all[1234:1241]) and torch.equal(i_few, i_all[1234:1241])
     sc, rule = oracle_args(entry, "sigmoid")
