@@ -22,7 +22,11 @@
 namespace moe_route {
 namespace {
 
-constexpr int kRowWaves = 4;  // waves (rows) per block
+// Waves (rows) per block: one up to kRowOneWaveTokens tokens, where blocks of
+// a single wave spread over more compute units and a call finishes sooner
+// (64 tokens: 3.06 against 3.25 µs a call, graph replay); four above.
+constexpr int kRowWaves = 4;
+constexpr int64_t kRowOneWaveTokens = 1024;
 
 template <typename T>
 __device__ __forceinline__ void load_row4(const T* __restrict__ p, int lane, float (&x)[4]);
@@ -47,8 +51,9 @@ __global__ __launch_bounds__(kRowWaves* kWave) void route_row_kernel(
     const T* __restrict__ logits, BiasRef bias, int64_t M, int TG, int K, int renorm,
     float* __restrict__ w_out, int32_t* __restrict__ id_out) {
     const int lane = threadIdx.x % kWave;
-    const int64_t stride = (int64_t)gridDim.x * kRowWaves;
-    int64_t row = (int64_t)blockIdx.x * kRowWaves + threadIdx.x / kWave;
+    const int waves = blockDim.x / kWave;  // 1 or kRowWaves
+    const int64_t stride = (int64_t)gridDim.x * waves;
+    int64_t row = (int64_t)blockIdx.x * waves + threadIdx.x / kWave;
 
     // The row's logits are requested first (a wave past the last row loads
     // that row and leaves), then the bias (4 entries a lane).
@@ -71,10 +76,11 @@ template <typename T, bool BIAS, int GRP>
 route_status_t launch_row(const RouteProblem& p) {
     auto kernel = route_row_kernel<T, BIAS, GRP>;
     static const int resident = resident_blocks(kernel, kRowWaves * kWave);
-    int64_t blocks = (p.M + kRowWaves - 1) / kRowWaves;
-    const int64_t cap = (int64_t)device_cu_count() * resident;
+    const int waves = p.M <= kRowOneWaveTokens ? 1 : kRowWaves;
+    int64_t blocks = (p.M + waves - 1) / waves;
+    const int64_t cap = (int64_t)device_cu_count() * resident * (kRowWaves / waves);
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kRowWaves * kWave), 0, p.stream,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(waves * kWave), 0, p.stream,
                        static_cast<const T*>(p.logits), p.bias, p.M, p.TG, p.K,
                        p.renorm ? 1 : 0, p.weights, p.ids);
     return hipGetLastError() == hipSuccess ? ROUTE_OK : ROUTE_ELAUNCH;
